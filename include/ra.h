@@ -1,0 +1,201 @@
+/*
+ * ra.h -- C ABI of the blockwise ring-attention step for AMD MI355X (gfx950).
+ *
+ * One rank's query chunk is attended against the key/value chunks of a sequence
+ * in ring order.  Each ring step is a tiled online softmax (running max and sum)
+ * that emits a partial output and its log-sum-exp (LSE); partials are merged by
+ * LSE, so the final result equals softmax(Q K^T * scale) V over the whole
+ * sequence ("Ring Attention & Friends": "Flash Attention - Tiling with the
+ * Softmax Rescaling Trick" and "Ring Attention"; Mosaic post, "How Ring Attention
+ * Works"; ringmaster page, "Layout": ring/loop.py, ring/merge.py).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * Shapes.  B = batch, Hq / Hkv = query / key-value heads (Hq % Hkv == 0, query
+ *    head h reads KV head h / (Hq/Hkv)), S = total sequence, p = ring size,
+ *    L = S / p tokens per chunk, D = head_dim_padded in {32, 64, 128}.
+ *  * Tensors in the problem dtype (q, every k and v chunk, out, dout) are
+ *    [B, H, L, D] with element strides (b, h, t) given in the problem and a unit
+ *    stride along D; every row must start 16-byte aligned.  Columns
+ *    head_dim..D-1 of q, k and v must be zero (storage padding).
+ *  * fp32 buffers (partial/accumulated outputs o, dq, dk, dv) are contiguous
+ *    [B, H, L, D]; lse and delta are contiguous [B, Hq, L].  LSE is the natural
+ *    log of sum_j exp(scaled score); a row that sees no key has o = 0 and
+ *    lse = -inf.
+ *  * Positions.  Token t of chunk c has global position pos(c, t):
+ *      RA_LAYOUT_CONTIGUOUS  c*L + t                    (dense shard)
+ *      RA_LAYOUT_STRIPED     t*p + c                    (token i in chunk i mod p)
+ *      RA_LAYOUT_ZIGZAG      with h = S/(2p): t < h -> c*h + t,
+ *                            else (2p-1-c)*h + (t-h)    (head/tail balancing)
+ *    (ringmaster page, "Layout": shard.py and balancers.py; "Ring Attention &
+ *    Friends", "Striped Attention").  With causal != 0, key u of chunk k is
+ *    visible to query t of chunk q iff pos(k, u) <= pos(q, t) (autoregressive,
+ *    diagonal included).
+ *  * Ownership.  The caller owns every buffer and the stream.  The library
+ *    allocates nothing, keeps no pointer after returning, and holds no per-call
+ *    state; calls on distinct streams are independent.
+ *  * Errors.  Every argument is validated before anything is enqueued; on
+ *    failure nothing is written and the status plus ra_last_error() (a
+ *    thread-local message) say why.  RA_OK means "enqueued": device faults
+ *    surface at the next synchronisation of the stream.  Unsupported inputs are
+ *    rejected up front, as the ringmaster page does for inputs it cannot handle
+ *    ("Native recurrent context parallelism": left padding, holes and arbitrary
+ *    masks are rejected).
+ */
+#ifndef RA_H
+#define RA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ra_status_t {
+  RA_OK = 0,
+  RA_ERR_NULL = 1,        /* a required pointer is NULL */
+  RA_ERR_SHAPE = 2,       /* sizes, strides, alignment or chunk ids are inconsistent */
+  RA_ERR_UNSUPPORTED = 3, /* valid but not implemented (dtype, head dim, mode) */
+  RA_ERR_WORKSPACE = 4,   /* workspace missing or too small */
+  RA_ERR_HIP = 5          /* a HIP runtime call failed at enqueue time */
+} ra_status_t;
+
+typedef enum ra_layout_t {
+  RA_LAYOUT_CONTIGUOUS = 0,
+  RA_LAYOUT_ZIGZAG = 1,
+  RA_LAYOUT_STRIPED = 2
+} ra_layout_t;
+
+typedef enum ra_dtype_t { RA_F32 = 0, RA_BF16 = 1 } ra_dtype_t;
+
+typedef enum ra_mode_t {
+  RA_WRITE = 0, /* write the step's normalised partial o and its lse */
+  RA_MERGE = 1  /* LSE-merge the step's partial into (o, lse) in place */
+} ra_mode_t;
+
+/* The problem one rank solves.  Plain data, copied by value into every launch. */
+typedef struct ra_problem_t {
+  int64_t batch;           /* B >= 1 */
+  int64_t heads_q;         /* Hq >= 1 */
+  int64_t heads_kv;        /* Hkv >= 1, Hq % Hkv == 0 */
+  int64_t head_dim;        /* true d (1..D); sets the default scale */
+  int64_t head_dim_padded; /* D in {32, 64, 128} (storage) */
+  int64_t seq_total;       /* S; S % p == 0 (S % 2p == 0 for zigzag); S < 2^31 */
+  int32_t world;           /* p >= 1 */
+  int32_t layout;          /* ra_layout_t */
+  int32_t causal;          /* 0 or 1 */
+  int32_t dtype;           /* ra_dtype_t of q, k, v, out, dout */
+  float scale;             /* 0 -> 1/sqrt(head_dim) */
+  int32_t reserved;        /* must be 0 */
+  int64_t q_stride[3];     /* (b, h, t) element strides of q */
+  int64_t kv_stride[3];    /* (b, h, t) element strides of every k and v chunk */
+  int64_t o_stride[3];     /* (b, h, t) element strides of out and dout */
+} ra_problem_t;
+
+/*
+ * One ring step, forward ("Ring Attention & Friends", "Flash Attention - Tiling
+ * with the Softmax Rescaling Trick"; Mosaic post, "How Ring Attention Works").
+ * q: [B, Hq, L, D] query chunk q_chunk.  k, v: [B, Hkv, L, D] KV chunk kv_chunk.
+ * o: fp32 [B, Hq, L, D], lse: fp32 [B, Hq, L] (contiguous, caller-owned).
+ * mode RA_WRITE: o, lse := the step's normalised partial output and its LSE
+ *   (rows that see no key of this chunk get 0 and -inf).
+ * mode RA_MERGE: (o, lse) := LSE-merge of (o, lse) with the step's partial; the
+ *   first step of a ring either uses RA_WRITE or starts from (0, -inf).
+ * The step's visible (query, key) tiles are computed from global positions and
+ * tiles with no visible pair are skipped.
+ */
+ra_status_t ra_block_attn_fwd(const ra_problem_t* prob, const void* q, int32_t q_chunk,
+                              const void* k, const void* v, int32_t kv_chunk, float* o,
+                              float* lse, int32_t mode, hipStream_t stream);
+
+/*
+ * In-place LSE merge of two partial results over disjoint key sets (ringmaster
+ * page, "Layout": ring/merge.py; Mosaic post, "How Ring Attention Works").
+ * o_acc, o_part: fp32 [rows, d]; lse_acc, lse_part: fp32 [rows] (contiguous).
+ *   lse := log(exp(lse_acc) + exp(lse_part))
+ *   o   := o_acc * exp(lse_acc - lse) + o_part * exp(lse_part - lse)
+ * A part with lse = -inf is the identity (the accumulator is left unchanged when
+ * lse_part = -inf).  d in 1..1024, d % 4 == 0; pointers 16-byte aligned.
+ */
+ra_status_t ra_lse_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc,
+                         const float* o_part, const float* lse_part, hipStream_t stream);
+
+/* Bytes of device workspace ra_ring_fwd needs (fp32 accumulator [B, Hq, L, D]). */
+ra_status_t ra_ring_workspace_size(const ra_problem_t* prob, size_t* bytes);
+
+/*
+ * The ring driver, forward, for rank `rank` (Mosaic post, "How Ring Attention
+ * Works": at step s the rank holds KV chunk (rank - s) mod p, having received it
+ * from rank - 1).  k_chunks[c] / v_chunks[c] is a HOST array of p device pointers
+ * indexed by chunk id.  Steps with no visible (query, key) pair are skipped.
+ * out: [B, Hq, L, D] in the problem dtype with o_stride; lse: fp32 [B, Hq, L].
+ * ws: device workspace of at least ra_ring_workspace_size() bytes, 256-byte
+ * aligned.  Partials are accumulated in fp32; out is rounded once at the end.
+ */
+ra_status_t ra_ring_fwd(const ra_problem_t* prob, int32_t rank, const void* q,
+                        const void* const* k_chunks, const void* const* v_chunks, void* out,
+                        float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Backward preprocess: delta[b, h, t] = sum_d dout[b, h, t, d] * out[b, h, t, d]
+ * (fp32), from the final forward output of this rank (ringmaster page, "Status":
+ * flash-style backward).  out, dout: [B, Hq, L, D] in the problem dtype, o_stride.
+ */
+ra_status_t ra_bwd_delta(const ra_problem_t* prob, const void* out, const void* dout,
+                         float* delta, hipStream_t stream);
+
+/*
+ * One ring step, backward: recompute P = exp(S * scale - lse) from the FINAL
+ * merged lse, then (ringmaster page, "Status": reverse-ring backward)
+ *   dv += P^T dO,  dP = dO V^T,  dS = P o (dP - delta),
+ *   dq += scale dS K,  dk += scale dS^T Q,
+ * with dk, dv of a KV head summed over the query heads of its group.
+ * dq: fp32 [B, Hq, L, D]; dk, dv: fp32 [B, Hkv, L, D]; all ACCUMULATED (+=) into
+ * caller-initialised buffers.  lse, delta: fp32 [B, Hq, L].
+ * Supported: bf16, D in {32, 64, 128}.
+ */
+ra_status_t ra_block_attn_bwd(const ra_problem_t* prob, const void* q, int32_t q_chunk,
+                              const void* k, const void* v, int32_t kv_chunk, const void* dout,
+                              const float* lse, const float* delta, float* dq, float* dk,
+                              float* dv, hipStream_t stream);
+
+/* Bytes of device workspace ra_ring_bwd needs (fp32 delta [B, Hq, L]). */
+ra_status_t ra_ring_bwd_workspace_size(const ra_problem_t* prob, size_t* bytes);
+
+/*
+ * The ring driver, backward, for rank `rank`: computes delta into ws, zero-fills
+ * dq and every dk_chunks[c], dv_chunks[c], then accumulates every step with a
+ * visible pair.  out / lse are the forward's results for this rank.  dk_chunks and
+ * dv_chunks are HOST arrays of p device pointers (fp32 [B, Hkv, L, D]); the result
+ * is this rank's share of the gradients (its queries only).
+ */
+ra_status_t ra_ring_bwd(const ra_problem_t* prob, int32_t rank, const void* q,
+                        const void* const* k_chunks, const void* const* v_chunks,
+                        const void* out, const void* dout, const float* lse, float* dq,
+                        float* const* dk_chunks, float* const* dv_chunks, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
+/* Host only.  host_out[t] = pos(chunk, t) for t in [0, L).  No device access. */
+ra_status_t ra_positions(const ra_problem_t* prob, int32_t chunk, int64_t* host_out);
+
+/*
+ * Host only.  Exact number of visible (query, key) pairs per (batch, query head)
+ * between query chunk q_chunk and KV chunk kv_chunk (L*L when not causal).
+ */
+ra_status_t ra_visible_pairs(const ra_problem_t* prob, int32_t q_chunk, int32_t kv_chunk,
+                             int64_t* pairs);
+
+/* Static string naming a status. */
+const char* ra_status_str(ra_status_t status);
+
+/* Thread-local message describing the last failure on this thread ("" if none). */
+const char* ra_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H */

@@ -179,12 +179,13 @@ def _visible_key_limit(q_pos_block: np.ndarray, causal: bool, seq_total: int) ->
 
 
 def attention_fwd(Qg, Kg, Vg, rows, causal: bool, scale: float | None = None,
-                  row_block: int = 256):
+                  row_block: int = 256, heads=None):
     """Exact attention of one rank's query rows against the whole global sequence.
 
     Qg [B, Hq, S, d], Kg / Vg [B, Hkv, S, d] in global token order; `rows` are the
     global positions of the rank's query rows (its share), in local order.
-    Returns O [B, Hq, len(rows), d] and LSE [B, Hq, len(rows)] in fp64.
+    `heads` optionally restricts the computation to those query heads (sampling).
+    Returns O [B, len(heads) or Hq, len(rows), d] and LSE [B, ..., len(rows)] in fp64.
     """
     B, Hq, S, d = Qg.shape
     Hkv = Kg.shape[1]
@@ -194,19 +195,19 @@ def attention_fwd(Qg, Kg, Vg, rows, causal: bool, scale: float | None = None,
         scale = _default_scale(d)
     rows = np.asarray(rows, dtype=np.int64)
     key_pos = np.arange(S, dtype=np.int64)
-    O = np.zeros((B, Hq, rows.size, Vg.shape[3]), dtype=np.float64)
-    LSE = np.full((B, Hq, rows.size), -np.inf, dtype=np.float64)
+    heads = list(range(Hq)) if heads is None else list(heads)
+    O = np.zeros((B, len(heads), rows.size, Vg.shape[3]), dtype=np.float64)
+    LSE = np.full((B, len(heads), rows.size), -np.inf, dtype=np.float64)
     for bi in range(B):
-        for h in range(Hq):
+        for hi, h in enumerate(heads):
             g = _kv_head(h, Hq, Hkv)
-            q = np.asarray(Qg[bi, h], dtype=np.float64)
             for a in range(0, rows.size, row_block):
                 rb = rows[a:a + row_block]
                 lim = _visible_key_limit(rb, causal, S)
-                o, l = attend(q[rb], Kg[bi, g, :lim], Vg[bi, g, :lim], rb,
+                o, l = attend(Qg[bi, h, rb], Kg[bi, g, :lim], Vg[bi, g, :lim], rb,
                               key_pos[:lim], causal, scale, row_block)
-                O[bi, h, a:a + rb.size] = o
-                LSE[bi, h, a:a + rb.size] = l
+                O[bi, hi, a:a + rb.size] = o
+                LSE[bi, hi, a:a + rb.size] = l
     return O, LSE
 
 
@@ -260,7 +261,7 @@ def lse_merge(o_a, lse_a, o_b, lse_b):
 # ----------------------------------------------------------------------------------
 
 def attention_bwd(Qg, Kg, Vg, dO_rows, rows, causal: bool, scale: float | None = None,
-                  row_block: int = 256):
+                  row_block: int = 256, heads=None):
     """Analytic gradient of l = sum_{i in rows} dO_i . O_i for one rank's query rows.
 
     With P the row softmax of the scaled, masked scores S:
@@ -274,7 +275,8 @@ def attention_bwd(Qg, Kg, Vg, dO_rows, rows, causal: bool, scale: float | None =
     Only this rank's rows contribute (the gradient share of one rank).
 
     Returns dQ [B, Hq, n, d] (rows in local order), dK and dV [B, Hkv, S, d] in
-    global order, all fp64.
+    global order, all fp64.  `heads` optionally restricts dQ to those query heads
+    (dO_rows then holds only those heads; dK and dV get only their contributions).
     """
     B, Hq, S, d = Qg.shape
     Hkv = Kg.shape[1]
@@ -282,20 +284,21 @@ def attention_bwd(Qg, Kg, Vg, dO_rows, rows, causal: bool, scale: float | None =
         scale = _default_scale(d)
     rows = np.asarray(rows, dtype=np.int64)
     key_pos = np.arange(S, dtype=np.int64)
-    dQ = np.zeros((B, Hq, rows.size, d), dtype=np.float64)
+    heads = list(range(Hq)) if heads is None else list(heads)
+    dQ = np.zeros((B, len(heads), rows.size, d), dtype=np.float64)
     dK = np.zeros((B, Hkv, S, d), dtype=np.float64)
     dV = np.zeros((B, Hkv, S, Vg.shape[3]), dtype=np.float64)
     for bi in range(B):
-        for h in range(Hq):
+        for hi, h in enumerate(heads):
             g = _kv_head(h, Hq, Hkv)
-            Qh = np.asarray(Qg[bi, h], dtype=np.float64)
+            Qh = Qg[bi, h]
             for a in range(0, rows.size, row_block):
                 rb = rows[a:a + row_block]
                 lim = _visible_key_limit(rb, causal, S)
-                q = Qh[rb]
+                q = np.asarray(Qh[rb], dtype=np.float64)
                 k = np.asarray(Kg[bi, g, :lim], dtype=np.float64)
                 v = np.asarray(Vg[bi, g, :lim], dtype=np.float64)
-                do = np.asarray(dO_rows[bi, h, a:a + rb.size], dtype=np.float64)
+                do = np.asarray(dO_rows[bi, hi, a:a + rb.size], dtype=np.float64)
                 s = (q @ k.T) * scale
                 if causal:
                     s = np.where(_visible(key_pos[:lim], rb), s, -np.inf)
@@ -306,7 +309,7 @@ def attention_bwd(Qg, Kg, Vg, dO_rows, rows, causal: bool, scale: float | None =
                 D = np.sum(do * O, axis=1)
                 dP = do @ v.T
                 dS = P * (dP - D[:, None])
-                dQ[bi, h, a:a + rb.size] = (dS @ k) * scale
+                dQ[bi, hi, a:a + rb.size] = (dS @ k) * scale
                 dK[bi, g, :lim] += (dS.T @ q) * scale
                 dV[bi, g, :lim] += P.T @ do
     return dQ, dK, dV

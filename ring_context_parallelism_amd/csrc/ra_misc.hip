@@ -1,0 +1,160 @@
+// Memory-bound helper kernels: the standalone LSE merge, the backward's
+// delta = rowsum(dO * O), and an fp32 fill (used instead of hipMemsetAsync so the
+// drivers stay capturable in HIP graphs).
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// One row of (o, lse) per group of G lanes; G divides 64, so a row never spans two
+// waves and every lane of a row reads lse_acc before the group leader rewrites it.
+template <int G>
+__global__ __launch_bounds__(256) void lse_merge_kernel(int64_t rows, int32_t d4, float* o_acc,
+                                                        float* lse_acc, const float* o_part,
+                                                        const float* lse_part) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / G;
+  const int c0 = (int)(gid % G);
+  if (row >= rows) return;
+  const float la = lse_acc[row], lp = lse_part[row];
+  if (lp == kNegInf) return;  // empty partial: identity
+  float wa, wp, lse;
+  if (la == kNegInf) {
+    wa = 0.0f;
+    wp = 1.0f;
+    lse = lp;
+  } else {
+    const float mx = fmaxf(la, lp);
+    const float ea = __expf(la - mx), ep = __expf(lp - mx);
+    const float den = ea + ep;
+    wa = ea / den;
+    wp = ep / den;
+    lse = mx + __logf(den);
+  }
+  f32x4* oa = (f32x4*)(o_acc + row * (int64_t)d4 * 4);
+  const f32x4* op = (const f32x4*)(o_part + row * (int64_t)d4 * 4);
+  for (int c = c0; c < d4; c += G) {
+    const f32x4 x = oa[c], y = op[c];
+    f32x4 r;
+    r[0] = x[0] * wa + y[0] * wp;
+    r[1] = x[1] * wa + y[1] * wp;
+    r[2] = x[2] * wa + y[2] * wp;
+    r[3] = x[3] * wa + y[3] * wp;
+    oa[c] = r;
+  }
+  if (c0 == 0) lse_acc[row] = lse;
+}
+
+// delta[row] = sum_d dout[row, d] * out[row, d]; one row per group of G lanes, each
+// lane reading 16 bytes of both tensors, then a butterfly reduction inside the group.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(int32_t B, int32_t H, int32_t L,
+                                                        const T* out, const T* dout, int64_t sb,
+                                                        int64_t sh, int64_t st, float* delta) {
+  constexpr int EPL = 16 / sizeof(T);  // elements per lane
+  constexpr int G = D / EPL;           // lanes per row
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / G;
+  const int c = (int)(gid % G);
+  const int64_t nrows = (int64_t)B * H * L;
+  float acc = 0.0f;
+  if (row < nrows) {
+    const int64_t t = row % L, bh = row / L;
+    const int64_t h = bh % H, b = bh / H;
+    const int64_t off = b * sb + h * sh + t * st + (int64_t)c * EPL;
+    if constexpr (sizeof(T) == 2) {
+      typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+      const bf16x8 x = *(const bf16x8*)(out + off);
+      const bf16x8 y = *(const bf16x8*)(dout + off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += (float)x[e] * (float)y[e];
+    } else {
+      const f32x4 x = *(const f32x4*)(out + off);
+      const f32x4 y = *(const f32x4*)(dout + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc += x[e] * y[e];
+    }
+  }
+#pragma unroll
+  for (int m = G / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (row < nrows && c == 0) delta[row] = acc;
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(float* p, int64_t n, float value) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n4 = n / 4;
+  if (i < n4) {
+    f32x4 v = {value, value, value, value};
+    ((f32x4*)p)[i] = v;
+  }
+  if (i < n - n4 * 4) p[n4 * 4 + i] = value;
+}
+
+template <typename T, int D>
+hipError_t delta_launch(int32_t B, int32_t H, int32_t L, const void* out, const void* dout,
+                        int64_t sb, int64_t sh, int64_t st, float* delta, hipStream_t s) {
+  constexpr int G = D / (16 / (int)sizeof(T));
+  const int64_t threads = (int64_t)B * H * L * G;
+  const int64_t blocks = (threads + 255) / 256;
+  hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, B, H, L,
+                     (const T*)out, (const T*)dout, sb, sh, st, delta);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_lse_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc,
+                            const float* o_part, const float* lse_part, hipStream_t s) {
+  const int32_t d4 = d / 4;
+  const int G = d4 <= 8 ? 8 : (d4 <= 16 ? 16 : (d4 <= 32 ? 32 : 64));
+  const int64_t threads = rows * G;
+  const int64_t blocks = (threads + 255) / 256;
+  if (rows == 0) return hipSuccess;
+  switch (G) {
+    case 8:
+      hipLaunchKernelGGL(lse_merge_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, s, rows, d4,
+                         o_acc, lse_acc, o_part, lse_part);
+      break;
+    case 16:
+      hipLaunchKernelGGL(lse_merge_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, s, rows, d4,
+                         o_acc, lse_acc, o_part, lse_part);
+      break;
+    case 32:
+      hipLaunchKernelGGL(lse_merge_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, s, rows, d4,
+                         o_acc, lse_acc, o_part, lse_part);
+      break;
+    default:
+      hipLaunchKernelGGL(lse_merge_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, rows, d4,
+                         o_acc, lse_acc, o_part, lse_part);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_delta(int dtype, int32_t B, int32_t H, int32_t L, int32_t D,
+                            const void* out, const void* dout, int64_t sb, int64_t sh,
+                            int64_t st, float* delta, hipStream_t s) {
+  if (dtype == RA_BF16) {
+    if (D == 128) return delta_launch<__bf16, 128>(B, H, L, out, dout, sb, sh, st, delta, s);
+    if (D == 64) return delta_launch<__bf16, 64>(B, H, L, out, dout, sb, sh, st, delta, s);
+    if (D == 32) return delta_launch<__bf16, 32>(B, H, L, out, dout, sb, sh, st, delta, s);
+  } else {
+    if (D == 128) return delta_launch<float, 128>(B, H, L, out, dout, sb, sh, st, delta, s);
+    if (D == 64) return delta_launch<float, 64>(B, H, L, out, dout, sb, sh, st, delta, s);
+    if (D == 32) return delta_launch<float, 32>(B, H, L, out, dout, sb, sh, st, delta, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t n4 = (n + 3) / 4;
+  const int64_t blocks = (n4 + 255) / 256;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, value);
+  return hipGetLastError();
+}
+
+}  // namespace ra

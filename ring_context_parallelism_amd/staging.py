@@ -1,0 +1,90 @@
+"""Places one rank's share of a workload in device memory (HBM).
+
+Takes the global-order host arrays of ``workloads.generate`` and builds the device
+tensors the C ABI consumes: the rank's query chunk, every KV chunk (indexed by
+chunk id), and dO for backward workloads, each [B, H, L, D] with the head dim
+zero-padded to D.  The token order inside each chunk comes from the library's own
+position map (``ra_positions``), so the host never re-implements the layouts.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+from . import ra
+from .workloads import Workload
+
+
+def problem_for(w: Workload, scale: float = 0.0) -> ra.Problem:
+    return ra.make_problem(batch=w.batch, heads_q=w.heads_q, heads_kv=w.heads_kv,
+                           head_dim=w.head_dim, head_dim_padded=w.head_dim_padded,
+                           seq_total=w.seq_total, world=w.world, layout=w.layout,
+                           causal=w.causal, dtype=w.dtype, scale=scale)
+
+
+def torch_dtype(w: Workload):
+    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+
+def _to_device(arr: np.ndarray, pos: np.ndarray, D: int, dtype, device) -> torch.Tensor:
+    """arr [B, H, S, d] (fp32, exact in dtype) -> device [B, H, len(pos), D] in dtype."""
+    B, H, _, d = arr.shape
+    host = torch.zeros((B, H, pos.size, D), dtype=torch.float32)
+    host[..., :d] = torch.from_numpy(np.ascontiguousarray(arr[:, :, pos, :]))
+    return host.to(dtype).to(device)
+
+
+@dataclasses.dataclass
+class Share:
+    prob: ra.Problem
+    q: torch.Tensor
+    k_chunks: list
+    v_chunks: list
+    do: torch.Tensor | None
+    rows: np.ndarray  # global positions of the rank's query rows (library map)
+
+
+def stage(w: Workload, arrays: dict, device="cuda", rank: int | None = None) -> Share:
+    prob = problem_for(w)
+    rank = w.rank if rank is None else rank
+    D, dt = w.head_dim_padded, torch_dtype(w)
+    rows = ra.ra_positions(prob, rank)
+    ks, vs = [], []
+    for c in range(w.world):
+        pos = ra.ra_positions(prob, c)
+        ks.append(_to_device(arrays["k"], pos, D, dt, device))
+        vs.append(_to_device(arrays["v"], pos, D, dt, device))
+    q = _to_device(arrays["q"], rows, D, dt, device)
+    do = _to_device(arrays["do"], rows, D, dt, device) if "do" in arrays else None
+    return Share(prob, q, ks, vs, do, rows)
+
+
+def ring_forward(share: Share, w: Workload, rank: int | None = None, stream=None):
+    """Runs ra_ring_fwd on a staged share; returns (out [B, Hq, L, D], lse fp32)."""
+    rank = w.rank if rank is None else rank
+    L, D = w.chunk_len, w.head_dim_padded
+    dev = share.q.device
+    out = torch.empty((w.batch, w.heads_q, L, D), dtype=torch_dtype(w), device=dev)
+    lse = torch.empty((w.batch, w.heads_q, L), dtype=torch.float32, device=dev)
+    ws = torch.empty(ra.ra_ring_workspace_size(share.prob) // 4, dtype=torch.float32, device=dev)
+    ra.ra_ring_fwd(share.prob, rank, share.q, share.k_chunks, share.v_chunks, out, lse, ws,
+                   stream=stream)
+    return out, lse
+
+
+def ring_backward(share: Share, w: Workload, out, lse, rank: int | None = None, stream=None):
+    """Runs ra_ring_bwd; returns (dq, dk_chunks, dv_chunks), fp32 [B, H, L, D]."""
+    rank = w.rank if rank is None else rank
+    L, D = w.chunk_len, w.head_dim_padded
+    dev = share.q.device
+    dq = torch.empty((w.batch, w.heads_q, L, D), dtype=torch.float32, device=dev)
+    dks = [torch.empty((w.batch, w.heads_kv, L, D), dtype=torch.float32, device=dev)
+           for _ in range(w.world)]
+    dvs = [torch.empty_like(dks[0]) for _ in range(w.world)]
+    ws = torch.empty(ra.ra_ring_bwd_workspace_size(share.prob) // 4, dtype=torch.float32,
+                     device=dev)
+    ra.ra_ring_bwd(share.prob, rank, share.q, share.k_chunks, share.v_chunks, out, share.do,
+                   lse, dq, dks, dvs, ws, stream=stream)
+    return dq, dks, dvs

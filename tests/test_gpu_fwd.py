@@ -1,0 +1,173 @@
+"""GPU parity of the forward path against the fp64 oracle, through the C ABI.
+
+* oracle-sized cases (several tiles plus a ragged tail, every layout, GQA, padded
+  head dims, fp32 and bf16): every rank's share of the ring forward, compared
+  element by element with the oracle's global result;
+* per-step partials (RA_WRITE) for every (query chunk, KV chunk) pair, including
+  rows that see nothing (0 and -inf), and RA_MERGE chains in ring order;
+* the standalone LSE merge against the oracle's merge, -inf rows included;
+* every workload at its full size through ra_ring_fwd (the launch configuration
+  the benchmark times), on sampled rows and heads the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ring_context_parallelism_amd import ra, staging
+from ring_context_parallelism_amd.workloads import WORKLOADS, Workload, generate
+from tests.gpu_util import assert_close, assert_lse, need_gpu, sample_heads, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(dtype, D, d, layout, p, S, causal, B, Hq, Hkv, dist="normal", scale=0.5, seed=100):
+    return Workload(f"t_{dtype}_{D}_{layout}", seed, dtype, B, Hq, Hkv, d, D, S, p, layout, 0,
+                    causal, dist, scale)
+
+
+SMALL = [
+    _wl("bf16", 128, 128, "contiguous", 2, 600, True, 2, 4, 2),
+    _wl("bf16", 128, 128, "striped", 3, 600, True, 1, 4, 1),
+    _wl("bf16", 128, 128, "zigzag", 2, 600, True, 1, 2, 2),
+    _wl("bf16", 128, 128, "striped", 2, 520, False, 1, 2, 1),
+    _wl("bf16", 128, 100, "contiguous", 1, 300, True, 1, 2, 1),
+    _wl("bf16", 64, 64, "zigzag", 3, 780, True, 1, 4, 2),
+    _wl("bf16", 32, 24, "contiguous", 4, 1000, False, 2, 4, 4, dist="uniform", scale=1.0),
+    _wl("f32", 64, 64, "contiguous", 4, 1024, True, 1, 1, 1, scale=1.0),
+    _wl("f32", 32, 24, "contiguous", 4, 1000, False, 2, 2, 2, dist="uniform", scale=1.0),
+    _wl("f32", 128, 128, "striped", 2, 520, True, 1, 2, 1),
+    _wl("f32", 64, 40, "zigzag", 2, 520, True, 1, 2, 2),
+]
+
+
+def _ids(w):
+    return f"{w.dtype}-D{w.head_dim_padded}d{w.head_dim}-{w.layout}-p{w.world}-S{w.seq_total}-" \
+           f"{'causal' if w.causal else 'full'}-B{w.batch}H{w.heads_q}x{w.heads_kv}"
+
+
+def _np(t):
+    return t.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("w", SMALL, ids=_ids)
+def test_ring_fwd_every_rank(w):
+    dev = need_gpu()
+    arrays = generate(w)
+    d = w.head_dim
+    for r in range(w.world):
+        say(f"ring_fwd {_ids(w)} rank {r}")
+        share = staging.stage(w, arrays, dev, rank=r)
+        out, lse = staging.ring_forward(share, w, rank=r)
+        torch.cuda.synchronize()
+        rows = oracle.positions(w.layout, w.seq_total, w.world, r)
+        assert np.array_equal(rows, share.rows)
+        O, LSE = oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal)
+        got = _np(out)
+        assert_close(got[..., :d], O, w.dtype, f"O rank {r}")
+        assert np.all(got[..., d:] == 0.0), "padded head-dim columns must stay exactly 0"
+        assert_lse(_np(lse), LSE, f"LSE rank {r}")
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[1], SMALL[5], SMALL[7], SMALL[10]], ids=_ids)
+def test_block_fwd_partials_and_merge(w):
+    """RA_WRITE partial of every (query chunk, KV chunk) pair, then an RA_MERGE chain."""
+    dev = need_gpu()
+    arrays = generate(w)
+    d, D, L = w.head_dim, w.head_dim_padded, w.chunk_len
+    scale = 1.0 / np.sqrt(d)
+    for cq in range(w.world):
+        share = staging.stage(w, arrays, dev, rank=cq)
+        qpos = oracle.positions(w.layout, w.seq_total, w.world, cq)
+        o_acc = torch.zeros((w.batch, w.heads_q, L, D), dtype=torch.float32, device=dev)
+        l_acc = torch.full((w.batch, w.heads_q, L), float("-inf"), dtype=torch.float32, device=dev)
+        for s, ck in enumerate(oracle.ring_schedule(cq, w.world)):
+            say(f"block_fwd {_ids(w)} q_chunk {cq} kv_chunk {ck}")
+            kpos = oracle.positions(w.layout, w.seq_total, w.world, ck)
+            o = torch.empty((w.batch, w.heads_q, L, D), dtype=torch.float32, device=dev)
+            lse = torch.empty((w.batch, w.heads_q, L), dtype=torch.float32, device=dev)
+            ra.ra_block_attn_fwd(share.prob, share.q, cq, share.k_chunks[ck], share.v_chunks[ck],
+                                 ck, o, lse, ra.RA_WRITE)
+            ra.ra_block_attn_fwd(share.prob, share.q, cq, share.k_chunks[ck], share.v_chunks[ck],
+                                 ck, o_acc, l_acc, ra.RA_MERGE)
+            torch.cuda.synchronize()
+            Op, Lp = oracle.attention_partial(arrays["q"][:, :, qpos], arrays["k"][:, :, kpos],
+                                              arrays["v"][:, :, kpos], qpos, kpos, w.causal,
+                                              scale, w.heads_q, w.heads_kv)
+            got = _np(o)
+            assert_close(got[..., :d], Op, "bf16" if w.dtype == "bf16" else "f32",
+                         f"partial ({cq},{ck})")
+            empty = np.isneginf(Lp)
+            assert np.all(got[empty] == 0.0), "rows with no visible key must be 0"
+            assert_lse(_np(lse), Lp, f"partial LSE ({cq},{ck})")
+        O, LSE = oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], qpos, w.causal)
+        assert_close(_np(o_acc)[..., :d], O, "bf16" if w.dtype == "bf16" else "f32",
+                     f"merge chain rank {cq}")
+        assert_lse(_np(l_acc), LSE, f"merge chain LSE rank {cq}")
+
+
+@pytest.mark.parametrize("rows,d", [(1, 4), (1000, 128), (777, 24), (4096, 64), (64, 1024)])
+def test_lse_merge_kernel(rows, d):
+    dev = need_gpu()
+    rng = np.random.default_rng(rows + d)
+    oa, op = rng.standard_normal((rows, d)), rng.standard_normal((rows, d))
+    la, lp = rng.standard_normal(rows) * 4, rng.standard_normal(rows) * 4
+    la[::7] = -np.inf
+    oa[::7] = 0.0
+    lp[::5] = -np.inf
+    op[::5] = 0.0
+    want_o, want_l = oracle.lse_merge(oa, la, op, lp)
+    t = lambda x: torch.tensor(x, dtype=torch.float32, device=dev)
+    goa, gla, gop, glp = t(oa), t(la), t(op), t(lp)
+    say(f"lse_merge rows {rows} d {d}")
+    ra.ra_lse_merge(rows, d, goa, gla, gop, glp)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(goa.cpu().numpy() - want_o)) < 1e-5
+    got_l = gla.cpu().numpy()
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(want_l))
+    fin = ~np.isneginf(want_l)
+    if fin.any():
+        assert np.max(np.abs(got_l[fin] - want_l[fin])) < 1e-5
+
+
+def test_ring_fwd_deterministic():
+    dev = need_gpu()
+    w = SMALL[1]
+    arrays = generate(w)
+    share = staging.stage(w, arrays, dev, rank=1)
+    o1, l1 = staging.ring_forward(share, w, rank=1)
+    o2, l2 = staging.ring_forward(share, w, rank=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+FULL = [WORKLOADS["tiny_fp32"], WORKLOADS["llama_share"], WORKLOADS["gqa_striped"],
+        WORKLOADS["tabular_rows"], WORKLOADS["tabular_rows"].with_dtype("bf16"),
+        WORKLOADS["zigzag_fwdbwd"]]
+
+
+@pytest.mark.parametrize("w", FULL, ids=lambda w: f"{w.name}-{w.dtype}")
+def test_full_size_forward_sampled(w):
+    dev = need_gpu()
+    say(f"full-size forward {w.name} {w.dtype}: generating inputs")
+    arrays = generate(w)
+    share = staging.stage(w, arrays, dev)
+    say(f"full-size forward {w.name} {w.dtype}: ra_ring_fwd")
+    out, lse = staging.ring_forward(share, w)
+    torch.cuda.synchronize()
+    L, d = w.chunk_len, w.head_dim
+    full = w.name == "tiny_fp32"
+    t_idx = np.arange(L) if full else sample_rows(L, seed=w.seed)
+    heads = list(range(w.heads_q)) if full else sample_heads(w.heads_q, seed=w.seed)
+    rows = oracle.positions(w.layout, w.seq_total, w.world, w.rank)[t_idx]
+    say(f"full-size forward {w.name}: oracle on {len(t_idx)} rows x {len(heads)} heads")
+    O, LSE = oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal,
+                                  heads=heads)
+    got = out[:, heads][:, :, torch.from_numpy(t_idx).to(dev)].float().cpu().numpy()
+    s = assert_close(got[..., :d], O, w.dtype, f"{w.name} O")
+    assert_lse(lse[:, heads][:, :, torch.from_numpy(t_idx).to(dev)].cpu().numpy(), LSE,
+               f"{w.name} LSE")
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    if d < w.head_dim_padded:
+        assert torch.all(out[..., d:] == 0)
+    say(f"full-size forward {w.name}: {s}")
