@@ -1,0 +1,239 @@
+"""Benchmark of the blockwise ring-attention step on one MI355X.
+
+One step = one pass of the whole hot path for one rank's share: the forward ring
+(ra_ring_fwd: every ring step's tiled online softmax with the fused LSE merge,
+final output rounded to bf16, LSE saved), then the backward (ra_bwd_delta, then
+ra_block_attn_bwd for every live ring step, recomputing P from the saved LSE).
+Default workload: 16 heads x d 128, S = 131072 in the zigzag layout over p = 2,
+rank 0, bf16 -- the only workload that exercises every step, forward and backward.
+
+Inputs are synthetic (seeded, see ring_context_parallelism_amd/workloads.py) and
+already resident in HBM when the timed region starts.  Timing uses HIP events on
+the stream the kernels are launched on.  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+F32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="zigzag_fwdbwd")
+    ap.add_argument("--dtype", default=None, help="override the workload dtype (f32|bf16)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the oracle sample")
+    return ap.parse_args()
+
+
+def step_flops(w, prob, ra):
+    """Algorithmic FLOP per live ring step: exact visible pairs x 4d (fwd), x 10d (bwd)."""
+    out = []
+    for s in range(w.world):
+        c = (w.rank - s) % w.world
+        pairs = ra.ra_visible_pairs(prob, w.rank, c)
+        if pairs == 0:
+            continue
+        bh = w.batch * w.heads_q
+        out.append(dict(step=s, chunk=c, visible_pairs_per_head=pairs,
+                        fwd_flop=4.0 * w.head_dim * pairs * bh,
+                        bwd_flop=10.0 * w.head_dim * pairs * bh))
+    return out
+
+
+def cpu_baseline(w, arrays, target_s):
+    """The oracle, as it is, on a bounded sample of the same share (fp64, host cores)."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas = ",".join(sorted({p.get("internal_api", "?") for p in threadpool_info()}))
+    except Exception:  # pragma: no cover - reporting only
+        threads, blas = 1, "unknown"
+    rows_all = oracle.positions(w.layout, w.seq_total, w.world, w.rank)
+    rng = np.random.default_rng(1234)
+    n = 64
+    while True:
+        t_idx = np.sort(rng.choice(rows_all.size, size=min(n, rows_all.size), replace=False))
+        rows = rows_all[t_idx]
+        t0 = time.perf_counter()
+        if w.backward:
+            dO = arrays["do"][:, :1][:, :, rows]
+            oracle.attention_bwd(arrays["q"], arrays["k"], arrays["v"], dO, rows, w.causal,
+                                 heads=[0])
+        oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal, heads=[0])
+        dt = time.perf_counter() - t0
+        if dt >= 0.6 * target_s or n >= rows_all.size:
+            break
+        # grow the sample towards the target wall time (at most 16x per round)
+        n = int(min(rows_all.size, n * min(16.0, max(2.0, target_s / max(dt, 1e-3)))))
+    pairs = float(np.sum(rows + 1)) if w.causal else float(rows.size * w.seq_total)
+    per_pair = (4.0 + (10.0 if w.backward else 0.0)) * w.head_dim
+    flop = pairs * per_pair * w.batch
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rows.size} query rows of head 0 (batch {w.batch}), "
+                      f"{'forward + backward' if w.backward else 'forward'} in fp64, "
+                      f"{pairs:.3e} visible pairs, {dt:.1f} s wall, BLAS {blas}",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU ring exchange is a design note, not part of this path).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from ring_context_parallelism_amd import ra, staging
+    from ring_context_parallelism_amd.workloads import WORKLOADS, generate
+
+    w = WORKLOADS[args.workload]
+    if args.dtype:
+        w = w.with_dtype(args.dtype)
+    dev = torch.device("cuda:0")
+    ra.lib()  # fail loudly if the library is missing
+    print(f"[bench] workload {w.name} {w.dtype}: generating inputs", file=sys.stderr, flush=True)
+    arrays = generate(w)
+    share = staging.stage(w, arrays, dev)
+    prob = share.prob
+    steps = step_flops(w, prob, ra)
+    L, D = w.chunk_len, w.head_dim_padded
+    stream = torch.cuda.current_stream()
+    tdt = staging.torch_dtype(w)
+
+    out = torch.empty((w.batch, w.heads_q, L, D), dtype=tdt, device=dev)
+    lse = torch.empty((w.batch, w.heads_q, L), dtype=torch.float32, device=dev)
+    ws = torch.empty(ra.ra_ring_workspace_size(prob) // 4, dtype=torch.float32, device=dev)
+    if w.backward:
+        delta = torch.empty((w.batch, w.heads_q, L), dtype=torch.float32, device=dev)
+        dq = torch.empty((w.batch, w.heads_q, L, D), dtype=torch.float32, device=dev)
+        dks = [torch.empty((w.batch, w.heads_kv, L, D), dtype=torch.float32, device=dev)
+               for _ in range(w.world)]
+        dvs = [torch.empty_like(dks[0]) for _ in range(w.world)]
+
+    n_ev = 2 + (1 + len(steps) if w.backward else 0)
+
+    def one_step(ev):
+        ev[0].record(stream)
+        ra.ra_ring_fwd(prob, w.rank, share.q, share.k_chunks, share.v_chunks, out, lse, ws,
+                       stream=stream)
+        ev[1].record(stream)
+        if not w.backward:
+            return
+        ra.ra_bwd_delta(prob, out, share.do, delta, stream=stream)
+        dq.zero_()
+        for c in range(w.world):
+            dks[c].zero_()
+            dvs[c].zero_()
+        ev[2].record(stream)
+        for i, st in enumerate(steps):
+            c = st["chunk"]
+            ra.ra_block_attn_bwd(prob, share.q, w.rank, share.k_chunks[c], share.v_chunks[c], c,
+                                 share.do, lse, delta, dq, dks[c], dvs[c], stream=stream)
+            ev[3 + i].record(stream)
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+              for _ in range(args.steps)]
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    warm = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for _ in range(args.warmup):
+        one_step(warm)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        one_step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    step_ms = np.array([e[0].elapsed_time(e[-1]) for e in events])
+    fwd_flop = sum(s["fwd_flop"] for s in steps)
+    bwd_flop = sum(s["bwd_flop"] for s in steps) if w.backward else 0.0
+    peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
+    ms_per_step = float(np.mean(step_ms))
+    value = (fwd_flop + bwd_flop) / (ms_per_step * 1e-3) / 1e12
+
+    fwd_step_ms = float(np.mean(fwd_ms)) / len(steps)  # the driver launches one kernel per live step
+    detail = []
+    for i, st in enumerate(steps):
+        d = dict(step=st["step"], chunk=st["chunk"],
+                 visible_pairs_per_head=st["visible_pairs_per_head"],
+                 fwd_ms_est=fwd_step_ms,
+                 fwd_tflops=st["fwd_flop"] / (fwd_step_ms * 1e-3) / 1e12)
+        if w.backward:
+            bms = np.array([e[2 + i].elapsed_time(e[3 + i]) for e in events])
+            d.update(bwd_ms=float(np.mean(bms)), bwd_ms_min=float(np.min(bms)),
+                     bwd_tflops=st["bwd_flop"] / (float(np.mean(bms)) * 1e-3) / 1e12)
+        d["fwd_pct_peak"] = 100.0 * d["fwd_tflops"] / peak
+        if w.backward:
+            d["bwd_pct_peak"] = 100.0 * d["bwd_tflops"] / peak
+        detail.append(d)
+
+    fwd_tflops = fwd_flop / (float(np.mean(fwd_ms)) * 1e-3) / 1e12
+    res = {
+        "metric": "causal-adjusted attention TFLOP/s per ring step (fwd, bwd) + % of MFMA peak",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q,
+                   "heads_kv": w.heads_kv, "head_dim": w.head_dim,
+                   "head_dim_padded": w.head_dim_padded, "seq_total": w.seq_total,
+                   "world": w.world, "layout": w.layout, "rank": w.rank, "causal": w.causal,
+                   "passes": "fwd+bwd" if w.backward else "fwd"},
+        "fwd": {"ms": round(float(np.mean(fwd_ms)), 4), "tflops": round(fwd_tflops, 3),
+                "pct_peak": round(100.0 * fwd_tflops / peak, 2), "flop": fwd_flop},
+        "per_step": detail,
+        "wall_s": round(wall, 3),
+    }
+    if w.backward:
+        bwd_ms_total = float(np.mean([e[2].elapsed_time(e[-1]) for e in events]))
+        aux_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+        bwd_tflops = bwd_flop / (bwd_ms_total * 1e-3) / 1e12
+        res["bwd"] = {"ms": round(bwd_ms_total, 4), "tflops": round(bwd_tflops, 3),
+                      "pct_peak": round(100.0 * bwd_tflops / peak, 2), "flop": bwd_flop,
+                      "delta_and_zero_ms": round(aux_ms, 4)}
+        # dominant kernel: the backward step kernel (one launch per live ring step)
+        per_launch_flop = bwd_flop / len(steps)
+        launch_ms = bwd_ms_total / len(steps)
+        name = "bwd_kernel"
+    else:
+        per_launch_flop = fwd_flop / len(steps)
+        launch_ms = fwd_step_ms
+        name = "fwd_kernel"
+    achieved = per_launch_flop / (launch_ms * 1e-3) / 1e12
+    res["roofline"] = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                       "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                       "kernel": name, "avg_launch_ms": round(launch_ms, 4),
+                       "flop_per_launch": per_launch_flop}
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, arrays, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
