@@ -74,6 +74,12 @@ ra_status_t check_problem(const ra_problem_t* p) {
                     names[i], j);
     }
   const int64_t L = p->seq_total / p->world;
+  // The kernels address rows inside one head with 32-bit buffer offsets (a tile may
+  // run up to 256 rows past the chunk end, where loads return zeros).
+  for (int i = 0; i < 2; ++i)
+    if ((L + 256) * strides[i][2] * es >= (int64_t(1) << 32))
+      return fail(RA_ERR_UNSUPPORTED, "%s[2] too large: one head's rows must span < 4 GiB",
+                  names[i]);
   const int64_t rows = p->batch * p->heads_q;
   if (rows * ((L + 127) / 128) >= (int64_t(1) << 31) || p->batch * p->heads_kv * L >= (int64_t(1) << 40))
     return fail(RA_ERR_SHAPE, "problem too large for one launch");

@@ -37,7 +37,17 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;
 
-__device__ inline float partner(float x) { return __shfl_xor(x, 32, 64); }
+// The two halves of a wave (lanes l and l ^ 32) hold the same query rows.
+// permlane32_swap returns (own, partner) in lanes < 32 and (partner, own) in lanes
+// >= 32, so a max or a sum of the pair needs no select.
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -62,7 +72,7 @@ template <int D>
 __device__ inline void fwd_epilogue(const FwdArgs& a, int b, int h, int tq, int hh,
                                     const RowState& st, f32x16 (&o_t)[D / 32]) {
   const int L = a.map.L;
-  const float l_tot = st.l + partner(st.l);
+  const float l_tot = pair_sum(st.l);
   const bool live = l_tot > 0.0f;
   const float lse_s = live ? (st.m * a.scale_log2 + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
   const float inv_l = live ? 1.0f / l_tot : 0.0f;
@@ -123,107 +133,74 @@ __device__ inline void fwd_epilogue(const FwdArgs& a, int b, int h, int tq, int 
 }
 
 // ------------------------------------------------------------------------- bf16 path
+//
+// K and V tiles go global -> LDS with direct-to-LDS buffer loads (no staging
+// registers): lane i of a load lands at tile + 16 i bytes, so each lane fetches
+// the global 16-byte chunk that belongs at its LDS slot, which realises the XOR
+// swizzles below.  Rows past the chunk end are outside the buffer resource and
+// arrive as zeros.  V stays row-major; the PV operand V^T is read with the LDS
+// transpose load (ds_read_b64_tr_b16).
 
-template <int D, int BN>
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+template <int D>
 struct Bf16Tile {
-  static constexpr int KCH = D / 8;                                     // 16B chunks per K row
-  static constexpr int KSW = (KCH < 8 ? KCH : 8) - 1;                   // K swizzle mask
-  static constexpr int VCH = BN / 8;                                    // 16B chunks per Vt row
-  static constexpr int VSW = (VCH < 8 ? VCH : 8) - 1;                   // Vt swizzle mask
-  static constexpr int NK = (BN * KCH + kThreads - 1) / kThreads;       // K chunks per thread
-  static constexpr int NVG = (BN / 4) * KCH;                            // 4-key x 8-d V groups
-  static constexpr int NV = (NVG + kThreads - 1) / kThreads;            // V groups per thread
+  static constexpr int KCH = D / 8;                    // 16-byte chunks per row
+  static constexpr int KSW = (KCH < 8 ? KCH : 8) - 1;  // K swizzle mask (b128 reads)
 };
 
-// Offset (elements) of 16B chunk `c` of K row `r` in the swizzled K tile.
-template <int D, int BN>
-__device__ inline int k_off(int r, int c) {
-  return r * D + ((c ^ (r & Bf16Tile<D, BN>::KSW)) << 3);
-}
-// Offset (elements) of chunk `c` of Vt row `d` (head-dim index) in the swizzled tile.
-template <int D, int BN>
-__device__ inline int vt_off(int d, int c) {
-  return d * BN + ((c ^ ((d ^ (d >> 3)) & Bf16Tile<D, BN>::VSW)) << 3);
-}
-// Key permutation inside a Vt row: swap bits 2 and 3 of the key index.
-__device__ inline int vt_col(int key) {
-  return (key & ~0xC) | ((key >> 1) & 0x4) | ((key << 1) & 0x8);
+// K tile: chunk c of key row r lives at chunk c ^ (r & KSW).
+template <int D>
+__device__ inline int k_swz(int r) { return r & Bf16Tile<D>::KSW; }
+// V tile: transpose reads touch 4 consecutive rows x 32 bytes; spread those rows
+// over distinct banks.
+template <int D>
+__device__ inline int v_swz(int r) {
+  return Bf16Tile<D>::KCH >= 8 ? ((r & 3) << 1) : (((r >> 1) & 1) << 1);
 }
 
+// Issues the direct-to-LDS loads of one BN x D tile (rows u0..u0+BN-1) of K and V.
 template <int D, int BN>
-struct Bf16Stage {
-  uint4 k[Bf16Tile<D, BN>::NK];
-  uint4 v[Bf16Tile<D, BN>::NV][4];
-};
-
-template <int D, int BN>
-__device__ inline void bf16_load(Bf16Stage<D, BN>& st, const __bf16* kb, const __bf16* vb,
-                                 int64_t kv_st, int u0, int L, int tid) {
-  using T = Bf16Tile<D, BN>;
+__device__ inline void dma_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                uint32_t row_bytes, int u0, __bf16* ks, __bf16* vs, int wave,
+                                int lane) {
+  constexpr int KCH = Bf16Tile<D>::KCH;
+  constexpr int SLOTS = BN * KCH;                  // 16-byte slots per tile
+  constexpr int NI = SLOTS / kThreads;             // loads per thread per tensor
+  static_assert(SLOTS % kThreads == 0, "tile must be a multiple of 256 slots");
 #pragma unroll
-  for (int it = 0; it < T::NK; ++it) {
-    const int ci = it * kThreads + tid;
-    const int r = ci / T::KCH, c = ci % T::KCH;
-    const int u = u0 + r;
-    uint4 z = {0u, 0u, 0u, 0u};
-    if (ci < BN * T::KCH && u < L) z = *(const uint4*)(kb + (int64_t)u * kv_st + c * 8);
-    st.k[it] = z;
-  }
-#pragma unroll
-  for (int it = 0; it < T::NV; ++it) {
-    const int gi = it * kThreads + tid;
-    const int kg = gi / T::KCH, dg = gi % T::KCH;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int u = u0 + kg * 4 + r;
-      uint4 z = {0u, 0u, 0u, 0u};
-      if (gi < T::NVG && u < L) z = *(const uint4*)(vb + (int64_t)u * kv_st + dg * 8);
-      st.v[it][r] = z;
-    }
-  }
-}
-
-__device__ inline uint32_t half_of(const uint4& w, int e) {
-  const uint32_t word = e < 2 ? w.x : (e < 4 ? w.y : (e < 6 ? w.z : w.w));
-  return (e & 1) ? (word >> 16) : (word & 0xFFFFu);
-}
-
-template <int D, int BN>
-__device__ inline void bf16_store(const Bf16Stage<D, BN>& st, __bf16* ks, __bf16* vts, int tid) {
-  using T = Bf16Tile<D, BN>;
-#pragma unroll
-  for (int it = 0; it < T::NK; ++it) {
-    const int ci = it * kThreads + tid;
-    const int r = ci / T::KCH, c = ci % T::KCH;
-    if (ci < BN * T::KCH) *(uint4*)(ks + k_off<D, BN>(r, c)) = st.k[it];
-  }
-#pragma unroll
-  for (int it = 0; it < T::NV; ++it) {
-    const int gi = it * kThreads + tid;
-    if (gi < T::NVG) {
-      const int kg = gi / T::KCH, dg = gi % T::KCH;
-      const int col = vt_col(kg * 4);
-      const int cchunk = col >> 3, within = col & 7;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = dg * 8 + e;
-        uint2 w;
-        w.x = half_of(st.v[it][0], e) | (half_of(st.v[it][1], e) << 16);
-        w.y = half_of(st.v[it][2], e) | (half_of(st.v[it][3], e) << 16);
-        *(uint2*)(vts + vt_off<D, BN>(d, cchunk) + within) = w;
-      }
-    }
+  for (int it = 0; it < NI; ++it) {
+    const int base = it * kThreads + wave * 64;    // first slot of this wave's load
+    const int slot = base + lane;
+    const int r = slot / KCH, pc = slot % KCH;
+    const uint32_t roff = (uint32_t)(u0 + r) * row_bytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(ks + base * 8), 16,
+                                             roff + (uint32_t)((pc ^ k_swz<D>(r)) * 16), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(vs + base * 8), 16,
+                                             roff + (uint32_t)((pc ^ v_swz<D>(r)) * 16), 0, 0, 0);
   }
 }
 
 template <int D, int BN>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
-  using T = Bf16Tile<D, BN>;
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int NKB = D / 16;  // 16-wide head-dim blocks of the QK^T contraction
   constexpr int ND = D / 32;   // 32-row head-dim blocks of O^T
   constexpr int NB = BN / 32;  // 32-key blocks per tile
-  __shared__ __attribute__((aligned(16))) __bf16 ks[2][BN * D];
-  __shared__ __attribute__((aligned(16))) __bf16 vts[2][D * BN];
+  constexpr float kRescale = 8.0f;  // lazy rescale threshold (log2 units): p <= 2^8
+  // Two distinct LDS objects per tensor (not one indexed array): the compiler can
+  // then prove that the loads into one buffer never alias the reads of the other
+  // and does not wait for the prefetch before computing on the current tile.
+  __shared__ __attribute__((aligned(16))) __bf16 ks0[BN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 ks1[BN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 vs0[BN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 vs1[BN * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -241,14 +218,18 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
   const __bf16* qb = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
   const __bf16* kb = (const __bf16*)a.k + (int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh;
   const __bf16* vb = (const __bf16*)a.v + (int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh;
+  const uint32_t q_row = (uint32_t)(a.q_st * 2), kv_row = (uint32_t)(a.kv_st * 2);
+  const __amdgpu_buffer_rsrc_t qr_ = make_rsrc(qb, (uint32_t)L * q_row);
+  const __amdgpu_buffer_rsrc_t kr_ = make_rsrc(kb, (uint32_t)L * kv_row);
+  const __amdgpu_buffer_rsrc_t vr_ = make_rsrc(vb, (uint32_t)L * kv_row);
 
-  // This lane's query row as the B operand of S^T = K Q^T.
+  // This lane's query row as the B operand of S^T = K Q^T (rows >= L read as 0).
   bf16x8 qr[NKB];
 #pragma unroll
   for (int kk = 0; kk < NKB; ++kk) {
-    bf16x8 z = {};
-    if (tq < L) z = *(const bf16x8*)(qb + (int64_t)tq * a.q_st + kk * 16 + hh * 8);
-    qr[kk] = z;
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+        qr_, (uint32_t)tq * q_row + (uint32_t)(kk * 32 + hh * 16), 0, 0);
+    qr[kk] = __builtin_bit_cast(bf16x8, w);
   }
 
   // Visible-key prefix of this row, and of the whole tile.
@@ -266,29 +247,33 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int n = 0; n < ND; ++n) o_t[n] = f32x16{};
 
-  Bf16Stage<D, BN> stage;
-  if (n_tiles > 0) {
-    bf16_load<D, BN>(stage, kb, vb, a.kv_st, 0, L, tid);
-    bf16_store<D, BN>(stage, ks[0], vts[0], tid);
-  }
+  if (n_tiles > 0) dma_tile<D, BN>(kr_, vr_, kv_row, 0, ks0, vs0, wave, lane);
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    __syncthreads();
-    if (j + 1 < n_tiles) bf16_load<D, BN>(stage, kb, vb, a.kv_st, (j + 1) * BN, L, tid);
+  // Transpose-read geometry: source lane s of each 16-lane group points at key row
+  // (s / 4) of a 4-row block and head-dim column 4 (s % 4) of the lane group's 16
+  // columns; lane j then receives 4 consecutive keys at column j.
+  const int src_row = (lane & 15) >> 2;
+  const int src_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+
+  // One tile: wait for its loads, start the next tile's loads into the other
+  // buffer, then QK^T, softmax and PV on this one.
+  auto tile = [&](int j, const __bf16* kt, const __bf16* vt, __bf16* kn, __bf16* vn) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile j landed
+    __syncthreads();                     // ... and every other wave's; tile j-1 is free
+    if (j + 1 < n_tiles) dma_tile<D, BN>(kr_, vr_, kv_row, (j + 1) * BN, kn, vn, wave, lane);
 
     // S^T for this tile: NB blocks of 32 keys x 32 queries.
     f32x16 s[NB];
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
-      f32x16 acc = {};
+    for (int blk = 0; blk < NB; ++blk) s[blk] = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < NKB; ++kk) {
-        const bf16x8 kop = *(const bf16x8*)(&ks[buf][k_off<D, BN>(blk * 32 + l32, kk * 2 + hh)]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qr[kk], acc, 0, 0, 0);
+    for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+        const int r = blk * 32 + l32;
+        const bf16x8 kop = *(const bf16x8*)(kt + r * D + (((kk * 2 + hh) ^ k_swz<D>(r)) << 3));
+        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qr[kk], s[blk], 0, 0, 0);
       }
-      s[blk] = acc;
-    }
 
     // Mask keys beyond this row's visible prefix (causal diagonal, ragged tail).
     const int u0 = j * BN;
@@ -302,44 +287,64 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs a) {
         }
     }
 
-    // Online softmax update.
-    float mx = s[0][0];
+    // Online softmax with lazy rescaling: the reference max only moves when the
+    // tile's max exceeds it by more than 2^kRescale in probability, so p <= 2^8.
+    float mx = kNegInf;
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[blk][i]);
-    mx = fmaxf(mx, partner(mx));
-    const float m_new = fmaxf(st.m, mx);
-    const float alpha = fast_exp2((st.m - m_new) * a.scale_log2);
-    st.m = m_new;
-    const float mc = m_new * a.scale_log2;
-    float lsum = 0.0f;
+    mx = pair_max(mx);
+    const bool grow = (mx - st.m) * a.scale_log2 > kRescale;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mx : st.m;
+      const float alpha = fast_exp2((st.m - m_new) * a.scale_log2);
+      st.m = m_new;
+      st.l *= alpha;
+#pragma unroll
+      for (int n = 0; n < ND; ++n) o_t[n] *= alpha;
+    }
+    const float mc = st.m * a.scale_log2;
+    float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four short chains instead of one long one
     bf16x8 pb[NB][2];
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float pv = fast_exp2(__builtin_fmaf(s[blk][i], a.scale_log2, -mc));
-        lsum += pv;
+        lsum[i & 3] += pv;
         pb[blk][i >> 3][i & 7] = (__bf16)pv;
       }
-    st.l = st.l * alpha + lsum;
-#pragma unroll
-    for (int n = 0; n < ND; ++n) o_t[n] *= alpha;
+    st.l += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
 
-    // O^T += V^T P^T.
+    // O^T += V^T P^T.  The A operand of block (blk, mm) holds keys
+    // blk*32 + mm*16 + {0..3, 8..11} + 4 hh, read with two transpose loads.
 #pragma unroll
-    for (int n = 0; n < ND; ++n)
+    for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk)
+      for (int mm = 0; mm < 2; ++mm) {
+        bf16x8 vop[ND];
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          const bf16x8 vop =
-              *(const bf16x8*)(&vts[buf][vt_off<D, BN>(n * 32 + l32, blk * 4 + mm * 2 + hh)]);
-          o_t[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[blk][mm], o_t[n], 0, 0, 0);
+        for (int n = 0; n < ND; ++n) {
+          s16x4 x[2];
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int r = blk * 32 + mm * 16 + half * 8 + hh * 4 + src_row;
+            const int col = n * 32 + src_col;
+            const __bf16* ptr = vt + r * D + ((((col >> 3) ^ v_swz<D>(r))) << 3) + (col & 7);
+            x[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)ptr);
+          }
+          vop[n] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7));
         }
+#pragma unroll
+        for (int n = 0; n < ND; ++n)
+          o_t[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[n], pb[blk][mm], o_t[n], 0, 0, 0);
+      }
+  };
 
-    if (j + 1 < n_tiles) bf16_store<D, BN>(stage, ks[buf ^ 1], vts[buf ^ 1], tid);
+  for (int j = 0; j < n_tiles; j += 2) {
+    tile(j, ks0, vs0, ks1, vs1);
+    if (j + 1 < n_tiles) tile(j + 1, ks1, vs1, ks0, vs0);
   }
 
   fwd_epilogue<D>(a, b, h, tq, hh, st, o_t);
@@ -458,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
     for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[blk][i]);
-    mx = fmaxf(mx, partner(mx));
+    mx = pair_max(mx);
     const float m_new = fmaxf(st.m, mx);
     const float alpha = fast_exp2((st.m - m_new) * a.scale_log2);
     st.m = m_new;
