@@ -80,6 +80,8 @@ ra_status_t check_problem(const ra_problem_t* p) {
     if ((L + 256) * strides[i][2] * es >= (int64_t(1) << 32))
       return fail(RA_ERR_UNSUPPORTED, "%s[2] too large: one head's rows must span < 4 GiB",
                   names[i]);
+  if ((L + 256) * p->head_dim_padded * 4 >= (int64_t(1) << 32))
+    return fail(RA_ERR_UNSUPPORTED, "chunk too long: one head's fp32 rows must span < 4 GiB");
   const int64_t rows = p->batch * p->heads_q;
   if (rows * ((L + 127) / 128) >= (int64_t(1) << 31) || p->batch * p->heads_kv * L >= (int64_t(1) << 40))
     return fail(RA_ERR_SHAPE, "problem too large for one launch");

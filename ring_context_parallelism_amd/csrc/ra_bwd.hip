@@ -10,16 +10,19 @@
 //  * one workgroup = 4 waves = 128 keys of one (batch, KV head); each wave owns 32
 //    keys, keeps their K and V rows in registers and accumulates dK^T and dV^T for
 //    them across every query head of the group and every visible query tile;
-//  * query tiles of 32 rows stream through double-buffered LDS, each stored both
-//    row-major (A operand of S = Q K^T and dP = dO V^T) and transposed with the
-//    accumulator's row permutation (A operand of dK^T = Q^T dS and dV^T = dO^T P);
+//  * query tiles of 32 rows (Q, dO, LSE, delta) are fetched with direct-to-LDS
+//    buffer loads into double-buffered LDS, stored once, row-major, with a swizzle
+//    that is bank-conflict free both for 16-byte row reads (A operands of
+//    S = Q K^T and dP = dO V^T) and for the LDS transpose reads that give Q^T and
+//    dO^T (A operands of dK^T = Q^T dS and dV^T = dO^T P);
 //  * scores are computed as S[q][key]: every lane holds one key and 16 query rows,
 //    so P and dS feed the dK/dV MFMAs straight from registers;
-//  * dS is exchanged through LDS (bf16, [q][key]) for dQ = dS K, which the four
-//    waves split by head-dim block / key range and add to global dQ with fp32
-//    atomics (several workgroups contribute to one query row);
-//  * causal: only query tiles that see at least one of the workgroup's keys are
-//    visited; the element mask runs only on tiles that straddle the diagonal.
+//  * dS^T goes to LDS (bf16) and dQ = dS K is computed with transpose reads of dS^T
+//    and of the workgroup's K tile; the four waves split dQ by head-dim block / key
+//    range and add it to global dQ with fp32 atomics;
+//  * rows past the chunk end read as zeros (Q = dO = delta = 0 gives dS = 0);
+//    causal: only query tiles that see one of the workgroup's keys are visited and
+//    the element mask runs only on tiles that straddle the diagonal.
 #include "ra_internal.h"
 
 namespace ra {
@@ -28,12 +31,15 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 constexpr int kThreads = 256;
 constexpr int kBN = 128;   // keys per workgroup
 constexpr int kBMq = 32;   // query rows per tile
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kDsStride = kBN + 8;  // padded dS row (bank-conflict free)
 
 __device__ inline int xcd_remap(int bid, int nblk) {
   const int xcd = bid & 7, slot = bid >> 3;
@@ -42,55 +48,78 @@ __device__ inline int xcd_remap(int bid, int nblk) {
   return rem * per + (xcd - rem) * (per - 1) + slot;
 }
 
-// Swap bits 2 and 3 of a row index: the order in which the 32x32 accumulator holds
-// rows, used as the column order of the transposed query tiles.
-__device__ inline int perm_col(int r) { return (r & ~0xC) | ((r >> 1) & 0x4) | ((r << 1) & 0x8); }
-
-template <int D>
-struct BwdTile {
-  static constexpr int KCH = D / 8;                     // 16B chunks per row-major row
-  static constexpr int KSW = (KCH < 8 ? KCH : 8) - 1;   // row-major swizzle mask
-  static constexpr int NG = (kBMq / 4) * KCH;           // 4-row x 8-col groups per tensor
-  static constexpr int NKG = (kBN / 4) * KCH;           // groups of the K^T tile
-};
-
-// Row-major [rows][D] tile: offset of 16B chunk c of row r.
-template <int D>
-__device__ inline int rm_off(int r, int c) {
-  return r * D + ((c ^ (r & BwdTile<D>::KSW)) << 3);
-}
-// Transposed query tile [D][32]: offset of chunk c (of 4) of row d.
-__device__ inline int qt_off(int d, int c) { return d * kBMq + ((c ^ ((d >> 1) & 3)) << 3); }
-// Transposed key tile [D][128]: offset of chunk c (of 16) of row d.
-__device__ inline int kt_off(int d, int c) { return d * kBN + ((c ^ ((d ^ (d >> 3)) & 7)) << 3); }
-
-__device__ inline uint32_t half_of(const uint4& w, int e) {
-  const uint32_t word = e < 2 ? w.x : (e < 4 ? w.y : (e < 6 ? w.z : w.w));
-  return (e & 1) ? (word >> 16) : (word & 0xFFFFu);
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
-template <int D>
-struct QStage {
-  uint4 rows[4];  // 4 consecutive query rows x 8 head-dim columns (Q or dO)
-  float lse2, delta;
-};
+// Swizzle (XOR on the 16-byte chunk index) of a row-major tile with rows of RB
+// bytes, conflict free for 16-byte reads of 8 consecutive rows and for transpose
+// reads of 4 consecutive rows x 32 bytes.
+template <int RB>
+__device__ inline int dual_swz(int r) {
+  if constexpr (RB >= 128) return ((r & 3) << 1) | ((r >> 2) & 1);
+  else return (((r >> 1) & 1) << 1) | ((r >> 2) & 1);
+}
+// Element offset of column `col` (a multiple of 4) of row r in a swizzled tile.
+template <int COLS>
+__device__ inline int tile_off(int r, int col) {
+  return r * COLS + ((((col >> 3) ^ dual_swz<COLS * 2>(r))) << 3) + (col & 7);
+}
+
+// Transpose read of a row-major bf16 tile: lane j of each 16-lane group receives
+// rows rbase..rbase+3 at column cbase16 + j, where the caller passes the row and
+// column of its own source slot (rbase + (lane&15)/4, cbase16 + 4*(lane&3)).
+template <int COLS>
+__device__ inline s16x4 tr_read(const __bf16* tile, int r, int col) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + tile_off<COLS>(r, col)));
+}
+
+__device__ inline bf16x8 cat(s16x4 a, s16x4 b) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Direct-to-LDS loads of a ROWS x COLS bf16 tile starting at row r0 (swizzled).
+template <int ROWS, int COLS>
+__device__ inline void dma_rows(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, int r0,
+                                __bf16* tile, int wave, int lane) {
+  constexpr int CH = COLS / 8;
+  constexpr int SLOTS = ROWS * CH;
+  static_assert(SLOTS % 64 == 0, "tile must be a multiple of 64 slots");
+#pragma unroll
+  for (int it = 0; it < (SLOTS + kThreads - 1) / kThreads; ++it) {
+    const int base = it * kThreads + wave * 64;
+    if (SLOTS % kThreads != 0 && base >= SLOTS) break;  // wave-uniform
+    const int slot = base + lane;
+    const int r = slot / CH, pc = slot % CH;
+    const uint32_t off = (uint32_t)(r0 + r) * row_bytes +
+                         (uint32_t)((pc ^ dual_swz<COLS * 2>(r)) * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + base * 8), 16, off, 0, 0, 0);
+  }
+}
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_bf16_kernel(BwdArgs a) {
-  using T = BwdTile<D>;
+__global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   constexpr int NKB = D / 16;   // 16-wide head-dim blocks (S and dP contractions)
   constexpr int NDB = D / 32;   // 32-row head-dim blocks (dK^T, dV^T, dQ)
   constexpr int WPD = 4 / NDB;  // waves sharing one dQ head-dim block
   constexpr int KSTEPS = kBN / 16 / WPD;
 
-  __shared__ __attribute__((aligned(16))) __bf16 s_q[2][kBMq * D];
-  __shared__ __attribute__((aligned(16))) __bf16 s_do[2][kBMq * D];
-  __shared__ __attribute__((aligned(16))) __bf16 s_qt[2][D * kBMq];
-  __shared__ __attribute__((aligned(16))) __bf16 s_dot[2][D * kBMq];
-  __shared__ __attribute__((aligned(16))) __bf16 s_kt[D * kBN];
-  __shared__ __attribute__((aligned(16))) __bf16 s_ds[kBMq * kDsStride];
-  __shared__ __attribute__((aligned(16))) float s_lse2[2][kBMq];
-  __shared__ __attribute__((aligned(16))) float s_delta[2][kBMq];
+  // Distinct LDS objects for the two buffers of each tensor (see the forward).
+  __shared__ __attribute__((aligned(16))) __bf16 q0[kBMq * D];
+  __shared__ __attribute__((aligned(16))) __bf16 q1[kBMq * D];
+  __shared__ __attribute__((aligned(16))) __bf16 do0[kBMq * D];
+  __shared__ __attribute__((aligned(16))) __bf16 do1[kBMq * D];
+  __shared__ __attribute__((aligned(16))) float ls0[64];  // LSE rows (upper half unused)
+  __shared__ __attribute__((aligned(16))) float ls1[64];
+  __shared__ __attribute__((aligned(16))) float dl0[64];  // delta rows
+  __shared__ __attribute__((aligned(16))) float dl1[64];
+  __shared__ __attribute__((aligned(16))) __bf16 s_k[kBN * D];     // K tile, row-major
+  __shared__ __attribute__((aligned(16))) __bf16 s_dst[kBN * kBMq];  // dS^T [key][q]
+
+  // An (empty) statement that names an AGPR marks the kernel as using AGPRs, so the
+  // MFMAs take their accumulator form: dK^T / dV^T then live in AGPRs and the VGPRs
+  // stay free for operands instead of holding spilled copies.
+  asm volatile("" ::: "a255");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -106,38 +135,17 @@ __global__ __launch_bounds__(kThreads) void bwd_bf16_kernel(BwdArgs a) {
 
   const __bf16* kb = (const __bf16*)a.k + (int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh;
   const __bf16* vb = (const __bf16*)a.v + (int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh;
+  const uint32_t kv_row = (uint32_t)(a.kv_st * 2);
+  const __amdgpu_buffer_rsrc_t kr_ = make_rsrc(kb, (uint32_t)L * kv_row);
+  const __amdgpu_buffer_rsrc_t vr_ = make_rsrc(vb, (uint32_t)L * kv_row);
 
   // This lane's K and V rows as B operands (S = Q K^T, dP = dO V^T).
   bf16x8 kreg[NKB], vreg[NKB];
 #pragma unroll
   for (int kk = 0; kk < NKB; ++kk) {
-    bf16x8 zk = {}, zv = {};
-    if (key_ok) {
-      zk = *(const bf16x8*)(kb + (int64_t)key * a.kv_st + kk * 16 + hh * 8);
-      zv = *(const bf16x8*)(vb + (int64_t)key * a.kv_st + kk * 16 + hh * 8);
-    }
-    kreg[kk] = zk;
-    vreg[kk] = zv;
-  }
-  // K^T of the workgroup's keys for dQ = dS K (B operand, k = key).
-  for (int gi = tid; gi < T::NKG; gi += kThreads) {
-    const int kg = gi % (kBN / 4), dg = gi / (kBN / 4);
-    uint4 r4[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int u = u0 + kg * 4 + r;
-      uint4 z = {0u, 0u, 0u, 0u};
-      if (u < L) z = *(const uint4*)(kb + (int64_t)u * a.kv_st + dg * 8);
-      r4[r] = z;
-    }
-    const int col = kg * 4;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint2 w;
-      w.x = half_of(r4[0], e) | (half_of(r4[1], e) << 16);
-      w.y = half_of(r4[2], e) | (half_of(r4[3], e) << 16);
-      *(uint2*)(s_kt + kt_off(dg * 8 + e, col >> 3) + (col & 7)) = w;
-    }
+    const uint32_t off = (uint32_t)key * kv_row + (uint32_t)(kk * 32 + hh * 16);
+    kreg[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kr_, off, 0, 0));
+    vreg[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vr_, off, 0, 0));
   }
 
   // Visible query range of this key tile.  Query t sees key u iff
@@ -164,135 +172,101 @@ __global__ __launch_bounds__(kThreads) void bwd_bf16_kernel(BwdArgs a) {
     dk_t[n] = f32x16{};
   }
 
-  // Staging of one query tile: threads [0, NG) load Q, [NG, 2 NG) load dO, and
-  // threads [0, 32) also load the tile's LSE and delta rows.
-  QStage<D> st;
   auto tile_of = [&](int it, int& h, int& t0) {
     h = g * a.group + it / per_head;
     t0 = (qt_first + it % per_head) * kBMq;
   };
-  auto load = [&](int it) {
+  // Direct-to-LDS loads of query tile `it`: Q and dO rows, LSE and delta.
+  auto dma_q = [&](int it, __bf16* qn, __bf16* don, float* lsn, float* dln) {
     int h, t0;
     tile_of(it, h, t0);
-    if (tid < 2 * T::NG) {
-      const bool is_do = tid >= T::NG;
-      const int gi = is_do ? tid - T::NG : tid;
-      const int qg = gi % (kBMq / 4), dg = gi / (kBMq / 4);
-      const __bf16* base;
-      int64_t st_t;
-      if (is_do) {
-        base = (const __bf16*)a.dout + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;
-        st_t = a.o_st;
-      } else {
-        base = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
-        st_t = a.q_st;
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = t0 + qg * 4 + r;
-        uint4 z = {0u, 0u, 0u, 0u};
-        if (t < L) z = *(const uint4*)(base + (int64_t)t * st_t + dg * 8);
-        st.rows[r] = z;
-      }
-    }
-    if (tid < kBMq) {
-      const int r = tid;
-      const int t = t0 + r;
-      const int64_t row = ((int64_t)b * a.Hq + h) * L + t;
-      // Rows past the chunk end get P = exp2(-inf) = 0 through an infinite LSE.
-      st.lse2 = t < L ? a.lse[row] * kLog2e : __builtin_huge_valf();
-      st.delta = t < L ? a.delta[row] : 0.0f;
-    }
-  };
-  auto store = [&](int buf) {
-    if (tid < 2 * T::NG) {
-      const bool is_do = tid >= T::NG;
-      const int gi = is_do ? tid - T::NG : tid;
-      const int qg = gi % (kBMq / 4), dg = gi / (kBMq / 4);
-      __bf16* rm = is_do ? s_do[buf] : s_q[buf];
-      __bf16* tr = is_do ? s_dot[buf] : s_qt[buf];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) *(uint4*)(rm + rm_off<D>(qg * 4 + r, dg)) = st.rows[r];
-      const int col = perm_col(qg * 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint2 w;
-        w.x = half_of(st.rows[0], e) | (half_of(st.rows[1], e) << 16);
-        w.y = half_of(st.rows[2], e) | (half_of(st.rows[3], e) << 16);
-        *(uint2*)(tr + qt_off(dg * 8 + e, col >> 3) + (col & 7)) = w;
-      }
-    }
-    if (tid < kBMq) {
-      const int r = tid;
-      s_lse2[buf][r] = st.lse2;
-      s_delta[buf][r] = st.delta;
+    const __bf16* qb = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
+    const __bf16* ob = (const __bf16*)a.dout + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;
+    const uint32_t q_row = (uint32_t)(a.q_st * 2), o_row = (uint32_t)(a.o_st * 2);
+    dma_rows<kBMq, D>(make_rsrc(qb, (uint32_t)L * q_row), q_row, t0, qn, wave, lane);
+    dma_rows<kBMq, D>(make_rsrc(ob, (uint32_t)L * o_row), o_row, t0, don, wave, lane);
+    if (wave < 2) {
+      const float* src = (wave == 0 ? a.lse : a.delta) + ((int64_t)b * a.Hq + h) * L;
+      // lanes >= 32 (and rows >= L) fall outside the resource and write zeros
+      const uint32_t off = lane < 32 ? (uint32_t)(t0 + lane) * 4u : 0xFFFFFFF0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(src, (uint32_t)L * 4u),
+                                               (lds_void_t*)(wave == 0 ? lsn : dln), 4, off,
+                                               0, 0, 0);
     }
   };
 
-  if (n_iter > 0) {
-    load(0);
-    store(0);
-  }
-
+  // Transpose-read source slot of this lane (see tr_read).
+  const int src_row = (lane & 15) >> 2;
+  const int src_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
   const int dq_blk = wave / WPD;
   const int dq_k0 = (wave % WPD) * KSTEPS;
 
-  for (int it = 0; it < n_iter; ++it) {
-    const int buf = it & 1;
+  auto step = [&](int it, const __bf16* qt, const __bf16* dot, const float* ls,
+                  const float* dl, __bf16* qn, __bf16* don, float* lsn, float* dln) {
     int h, t0;
     tile_of(it, h, t0);
-    __syncthreads();  // tile `it` staged; every wave is done with s_ds of it-1
-    if (it + 1 < n_iter) load(it + 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile `it`
+    __syncthreads();                     // every wave's loads; tile it-1 and dS^T free
+    if (it + 1 < n_iter) dma_q(it + 1, qn, don, lsn, dln);
 
     // S[q][key] and dP[q][key] for this wave's 32 keys.
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {
-      const bf16x8 qa = *(const bf16x8*)(&s_q[buf][rm_off<D>(l32, kk * 2 + hh)]);
-      const bf16x8 da = *(const bf16x8*)(&s_do[buf][rm_off<D>(l32, kk * 2 + hh)]);
+      const bf16x8 qa = *(const bf16x8*)(qt + tile_off<D>(l32, kk * 16 + hh * 8));
+      const bf16x8 da = *(const bf16x8*)(dot + tile_off<D>(l32, kk * 16 + hh * 8));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[kk], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[kk], dp, 0, 0, 0);
     }
 
-    // P = exp2(S * scale_log2 - LSE * log2 e); dS = P (dP - delta).
+    __builtin_amdgcn_sched_barrier(0);
+    // P = exp2(S * scale_log2 - LSE * log2 e); dS = P (dP - delta).  Accumulator
+    // slot i holds query row gq*8 + hh*4 + e with i = gq*4 + e.
     const bool need_mask = t0 < t_mask_hi;
     bf16x8 pb[2], dsb[2];
-    float dsv[16];
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      const f32x4 l4 = *(const f32x4*)(&s_lse2[buf][gq * 8 + hh * 4]);
-      const f32x4 d4 = *(const f32x4*)(&s_delta[buf][gq * 8 + hh * 4]);
+      const f32x4 l4 = *(const f32x4*)(ls + gq * 8 + hh * 4);
+      const f32x4 d4 = *(const f32x4*)(dl + gq * 8 + hh * 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = gq * 4 + e;
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.scale_log2, -l4[e]));
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.scale_log2, -l4[e] * kLog2e));
         if (need_mask && t0 + gq * 8 + hh * 4 + e < t_min_lane) p = 0.0f;
         const float ds = p * (dp[i] - d4[e]);
         pb[i >> 3][i & 7] = (__bf16)p;
         dsb[i >> 3][i & 7] = (__bf16)ds;
-        dsv[i] = ds;
       }
     }
 
-    // dV^T += dO^T P and dK^T += Q^T dS (k = query rows, in accumulator order).
+    __builtin_amdgcn_sched_barrier(0);
+    // dV^T += dO^T P and dK^T += Q^T dS.  The A operands hold query rows
+    // mm*16 + {0..3, 8..11} + 4 hh (the accumulator order), read transposed.
 #pragma unroll
-    for (int n = 0; n < NDB; ++n)
+    for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        const bf16x8 doa = *(const bf16x8*)(&s_dot[buf][qt_off(n * 32 + l32, mm * 2 + hh)]);
-        const bf16x8 qta = *(const bf16x8*)(&s_qt[buf][qt_off(n * 32 + l32, mm * 2 + hh)]);
+      for (int n = 0; n < NDB; ++n) {
+        const int r0 = mm * 16 + hh * 4 + src_row;
+        const int col = n * 32 + src_col;
+        const bf16x8 doa = cat(tr_read<D>(dot, r0, col), tr_read<D>(dot, r0 + 8, col));
+        const bf16x8 qta = cat(tr_read<D>(qt, r0, col), tr_read<D>(qt, r0 + 8, col));
         dv_t[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doa, pb[mm], dv_t[n], 0, 0, 0);
         dk_t[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, dsb[mm], dk_t[n], 0, 0, 0);
       }
 
-    // dS to LDS as [q][key] for the dQ contraction.
+    __builtin_amdgcn_sched_barrier(0);
+    // dS^T[key][q] to LDS: this lane's 16 query rows are 4 runs of 4 consecutive
+    // rows, i.e. 32-bit word pairs of the packed dS vectors (whole words are
+    // stored, no 16-bit element shuffling).
     {
-      __bf16* row = s_ds + wave * 32 + l32;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = (i >> 2) * 8 + hh * 4 + (i & 3);
-        row[q * kDsStride] = (__bf16)dsv[i];
-      }
+      const int krow = wave * 32 + l32;
+      const u32x4 w0 = __builtin_bit_cast(u32x4, dsb[0]);
+      const u32x4 w1 = __builtin_bit_cast(u32x4, dsb[1]);
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      *(u32x2*)(s_dst + tile_off<kBMq>(krow, 0 * 8 + hh * 4)) = u32x2{w0[0], w0[1]};
+      *(u32x2*)(s_dst + tile_off<kBMq>(krow, 1 * 8 + hh * 4)) = u32x2{w0[2], w0[3]};
+      *(u32x2*)(s_dst + tile_off<kBMq>(krow, 2 * 8 + hh * 4)) = u32x2{w1[0], w1[1]};
+      *(u32x2*)(s_dst + tile_off<kBMq>(krow, 3 * 8 + hh * 4)) = u32x2{w1[2], w1[3]};
     }
     __syncthreads();
 
@@ -301,20 +275,31 @@ __global__ __launch_bounds__(kThreads) void bwd_bf16_kernel(BwdArgs a) {
       f32x16 acc = {};
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int k0 = (dq_k0 + ks) * 16;
-        const bf16x8 dsa = *(const bf16x8*)(&s_ds[l32 * kDsStride + k0 + hh * 8]);
-        const bf16x8 ktb = *(const bf16x8*)(&s_kt[kt_off(dq_blk * 32 + l32, (k0 >> 3) + hh)]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsa, ktb, acc, 0, 0, 0);
+        const int k0 = (dq_k0 + ks) * 16 + hh * 8 + src_row;
+        const bf16x8 dsa = cat(tr_read<kBMq>(s_dst, k0, src_col), tr_read<kBMq>(s_dst, k0 + 4, src_col));
+        const int col = dq_blk * 32 + src_col;
+        const bf16x8 kbv = cat(tr_read<D>(s_k, k0, col), tr_read<D>(s_k, k0 + 4, col));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsa, kbv, acc, 0, 0, 0);
       }
-      float* dqb = a.dq + (((int64_t)b * a.Hq + h) * L) * D + dq_blk * 32 + l32;
+      // Rows past the chunk end fall outside the resource and are dropped.
+      const __amdgpu_buffer_rsrc_t dqr =
+          make_rsrc(a.dq + (((int64_t)b * a.Hq + h) * L) * D, (uint32_t)L * D * 4u);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int t = t0 + (i >> 2) * 8 + hh * 4 + (i & 3);
-        if (t < L) atomicAdd(dqb + (int64_t)t * D, acc[i] * a.scale);
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+            acc[i] * a.scale, dqr, (uint32_t)(t * D + dq_blk * 32 + l32) * 4u, 0, 0);
       }
     }
+  };
 
-    if (it + 1 < n_iter) store(buf ^ 1);
+  if (n_iter > 0) {
+    dma_rows<kBN, D>(kr_, kv_row, u0, s_k, wave, lane);  // B operand of dQ = dS K
+    dma_q(0, q0, do0, ls0, dl0);
+  }
+  for (int it = 0; it < n_iter; it += 2) {
+    step(it, q0, do0, ls0, dl0, q1, do1, ls1, dl1);
+    if (it + 1 < n_iter) step(it + 1, q1, do1, ls1, dl1, q0, do0, ls0, dl0);
   }
 
   // dK, dV of this lane's key: accumulator rows are head-dim indices
