@@ -8,8 +8,9 @@
 //
 // Work decomposition (gfx950, wave64, 32x32x16 bf16 MFMA):
 //  * one workgroup = 4 waves = 128 keys of one (batch, KV head); each wave owns 32
-//    keys, keeps their K and V rows in registers and accumulates dK^T and dV^T for
-//    them across every query head of the group and every visible query tile;
+//    keys and accumulates dK^T and dV^T for them (in the accumulation registers)
+//    across every query head of the group and every visible query tile; the
+//    workgroup's K and V tiles stay in LDS for the whole launch;
 //  * query tiles of 32 rows (Q, dO, LSE, delta) are fetched with direct-to-LDS
 //    buffer loads into double-buffered LDS, stored once, row-major, with a swizzle
 //    that is bank-conflict free both for 16-byte row reads (A operands of
@@ -52,47 +53,46 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
-// Swizzle (XOR on the 16-byte chunk index) of a row-major tile with rows of RB
-// bytes, conflict free for 16-byte reads of 8 consecutive rows and for transpose
-// reads of 4 consecutive rows x 32 bytes.
-template <int RB>
-__device__ inline int dual_swz(int r) {
-  if constexpr (RB >= 128) return ((r & 3) << 1) | ((r >> 2) & 1);
-  else return (((r >> 1) & 1) << 1) | ((r >> 2) & 1);
-}
-// Element offset of column `col` (a multiple of 4) of row r in a swizzled tile.
+// Padded row-major tiles.  LDS serves 16 lanes x 16 bytes per clock from 64 banks;
+// a row stride of 3 or 13 (mod 16) sixteen-byte chunks makes both access patterns
+// of these tiles conflict free -- 16-byte reads of 16 consecutive rows at one
+// column (MFMA row operands) and transpose reads of 4 consecutive rows x 32 bytes
+// (MFMA transposed operands) -- and, unlike an XOR swizzle, keeps every address a
+// per-lane base plus a compile-time offset.
 template <int COLS>
-__device__ inline int tile_off(int r, int col) {
-  return r * COLS + ((((col >> 3) ^ dual_swz<COLS * 2>(r))) << 3) + (col & 7);
-}
+struct Pad {
+  static constexpr int CH = COLS / 8;  // data chunks per row
+  static constexpr int SCH = CH <= 3 ? 3 : (CH <= 13 ? 13 : (CH <= 19 ? 19 : 29));
+  static constexpr int PS = SCH * 8;   // row stride in elements
+  // 16-byte slots of a ROWS-row tile, rounded up to whole wave loads
+  static constexpr int slots(int rows) { return ((rows * SCH + 63) / 64) * 64; }
+};
 
-// Transpose read of a row-major bf16 tile: lane j of each 16-lane group receives
-// rows rbase..rbase+3 at column cbase16 + j, where the caller passes the row and
-// column of its own source slot (rbase + (lane&15)/4, cbase16 + 4*(lane&3)).
-template <int COLS>
-__device__ inline s16x4 tr_read(const __bf16* tile, int r, int col) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + tile_off<COLS>(r, col)));
+// Transpose read of a padded bf16 tile: lane j of each 16-lane group receives 4
+// consecutive rows at one column; `p` is this lane's own source slot.
+__device__ inline s16x4 tr_read(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
 }
 
 __device__ inline bf16x8 cat(s16x4 a, s16x4 b) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Direct-to-LDS loads of a ROWS x COLS bf16 tile starting at row r0 (swizzled).
+// Direct-to-LDS loads of rows r0..r0+ROWS-1 (COLS bf16 each) into a padded tile.
+// Pad slots, rows past ROWS and rows past the resource end are loaded as zeros.
 template <int ROWS, int COLS>
 __device__ inline void dma_rows(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, int r0,
                                 __bf16* tile, int wave, int lane) {
-  constexpr int CH = COLS / 8;
-  constexpr int SLOTS = ROWS * CH;
-  static_assert(SLOTS % 64 == 0, "tile must be a multiple of 64 slots");
+  using P = Pad<COLS>;
+  constexpr int SLOTS = P::slots(ROWS);
 #pragma unroll
   for (int it = 0; it < (SLOTS + kThreads - 1) / kThreads; ++it) {
     const int base = it * kThreads + wave * 64;
     if (SLOTS % kThreads != 0 && base >= SLOTS) break;  // wave-uniform
     const int slot = base + lane;
-    const int r = slot / CH, pc = slot % CH;
-    const uint32_t off = (uint32_t)(r0 + r) * row_bytes +
-                         (uint32_t)((pc ^ dual_swz<COLS * 2>(r)) * 16);
+    const int r = slot / P::SCH, c = slot % P::SCH;
+    const uint32_t off = (c < P::CH && r < ROWS) ? (uint32_t)(r0 + r) * row_bytes + (uint32_t)c * 16u
+                                                 : 0xFFFFFFF0u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + base * 8), 16, off, 0, 0, 0);
   }
 }
@@ -104,17 +104,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   constexpr int WPD = 4 / NDB;  // waves sharing one dQ head-dim block
   constexpr int KSTEPS = kBN / 16 / WPD;
 
+  using PD = Pad<D>;      // Q, dO, K, V tiles
+  using PT = Pad<kBMq>;   // dS^T tile
+  constexpr int PS = PD::PS, PST = PT::PS;
+  constexpr int QEL = PD::slots(kBMq) * 8, KEL = PD::slots(kBN) * 8, TEL = PT::slots(kBN) * 8;
+
   // Distinct LDS objects for the two buffers of each tensor (see the forward).
-  __shared__ __attribute__((aligned(16))) __bf16 q0[kBMq * D];
-  __shared__ __attribute__((aligned(16))) __bf16 q1[kBMq * D];
-  __shared__ __attribute__((aligned(16))) __bf16 do0[kBMq * D];
-  __shared__ __attribute__((aligned(16))) __bf16 do1[kBMq * D];
+  __shared__ __attribute__((aligned(16))) __bf16 q0[QEL];
+  __shared__ __attribute__((aligned(16))) __bf16 q1[QEL];
+  __shared__ __attribute__((aligned(16))) __bf16 do0[QEL];
+  __shared__ __attribute__((aligned(16))) __bf16 do1[QEL];
   __shared__ __attribute__((aligned(16))) float ls0[64];  // LSE rows (upper half unused)
   __shared__ __attribute__((aligned(16))) float ls1[64];
   __shared__ __attribute__((aligned(16))) float dl0[64];  // delta rows
   __shared__ __attribute__((aligned(16))) float dl1[64];
-  __shared__ __attribute__((aligned(16))) __bf16 s_k[kBN * D];     // K tile, row-major
-  __shared__ __attribute__((aligned(16))) __bf16 s_dst[kBN * kBMq];  // dS^T [key][q]
+  __shared__ __attribute__((aligned(16))) __bf16 s_k[KEL];    // K tile
+  __shared__ __attribute__((aligned(16))) __bf16 s_v[KEL];    // V tile
+  __shared__ __attribute__((aligned(16))) __bf16 s_dst[TEL];  // dS^T [key][q]
 
   // An (empty) statement that names an AGPR marks the kernel as using AGPRs, so the
   // MFMAs take their accumulator form: dK^T / dV^T then live in AGPRs and the VGPRs
@@ -138,15 +144,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
   const uint32_t kv_row = (uint32_t)(a.kv_st * 2);
   const __amdgpu_buffer_rsrc_t kr_ = make_rsrc(kb, (uint32_t)L * kv_row);
   const __amdgpu_buffer_rsrc_t vr_ = make_rsrc(vb, (uint32_t)L * kv_row);
-
-  // This lane's K and V rows as B operands (S = Q K^T, dP = dO V^T).
-  bf16x8 kreg[NKB], vreg[NKB];
-#pragma unroll
-  for (int kk = 0; kk < NKB; ++kk) {
-    const uint32_t off = (uint32_t)key * kv_row + (uint32_t)(kk * 32 + hh * 16);
-    kreg[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kr_, off, 0, 0));
-    vreg[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vr_, off, 0, 0));
-  }
 
   // Visible query range of this key tile.  Query t sees key u iff
   // pos(cq, t) >= pos(ck, u), i.e. t >= count_le(cq, pos(ck, u) - 1).
@@ -172,9 +169,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     dk_t[n] = f32x16{};
   }
 
+  // Query-tile order, rotated per key tile: workgroups of neighbouring key tiles
+  // would otherwise walk the same query tiles in lockstep and contend for the same
+  // dQ rows in their atomic adds.
+  const int rot = per_head > 0 ? (kt * 5) % per_head : 0;
   auto tile_of = [&](int it, int& h, int& t0) {
     h = g * a.group + it / per_head;
-    t0 = (qt_first + it % per_head) * kBMq;
+    int qi = it % per_head + rot;
+    if (qi >= per_head) qi -= per_head;
+    t0 = (qt_first + qi) * kBMq;
   };
   // Direct-to-LDS loads of query tile `it`: Q and dO rows, LSE and delta.
   auto dma_q = [&](int it, __bf16* qn, __bf16* don, float* lsn, float* dln) {
@@ -211,12 +214,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
 
     // S[q][key] and dP[q][key] for this wave's 32 keys.
     f32x16 s = {}, dp = {};
+    const int krow = wave * 32 + l32;
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {
-      const bf16x8 qa = *(const bf16x8*)(qt + tile_off<D>(l32, kk * 16 + hh * 8));
-      const bf16x8 da = *(const bf16x8*)(dot + tile_off<D>(l32, kk * 16 + hh * 8));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[kk], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[kk], dp, 0, 0, 0);
+      const int col = kk * 16 + hh * 8;
+      const bf16x8 qa = *(const bf16x8*)(qt + l32 * PS + col);
+      const bf16x8 da = *(const bf16x8*)(dot + l32 * PS + col);
+      const bf16x8 kbv = *(const bf16x8*)(s_k + krow * PS + col);
+      const bf16x8 vbv = *(const bf16x8*)(s_v + krow * PS + col);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kbv, s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vbv, dp, 0, 0, 0);
     }
 
     __builtin_amdgcn_sched_barrier(0);
@@ -246,10 +253,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
       for (int n = 0; n < NDB; ++n) {
-        const int r0 = mm * 16 + hh * 4 + src_row;
-        const int col = n * 32 + src_col;
-        const bf16x8 doa = cat(tr_read<D>(dot, r0, col), tr_read<D>(dot, r0 + 8, col));
-        const bf16x8 qta = cat(tr_read<D>(qt, r0, col), tr_read<D>(qt, r0 + 8, col));
+        const int o = (mm * 16 + hh * 4 + src_row) * PS + n * 32 + src_col;
+        const bf16x8 doa = cat(tr_read(dot + o), tr_read(dot + o + 8 * PS));
+        const bf16x8 qta = cat(tr_read(qt + o), tr_read(qt + o + 8 * PS));
         dv_t[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doa, pb[mm], dv_t[n], 0, 0, 0);
         dk_t[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, dsb[mm], dk_t[n], 0, 0, 0);
       }
@@ -259,14 +265,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     // rows, i.e. 32-bit word pairs of the packed dS vectors (whole words are
     // stored, no 16-bit element shuffling).
     {
-      const int krow = wave * 32 + l32;
       const u32x4 w0 = __builtin_bit_cast(u32x4, dsb[0]);
       const u32x4 w1 = __builtin_bit_cast(u32x4, dsb[1]);
       typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-      *(u32x2*)(s_dst + tile_off<kBMq>(krow, 0 * 8 + hh * 4)) = u32x2{w0[0], w0[1]};
-      *(u32x2*)(s_dst + tile_off<kBMq>(krow, 1 * 8 + hh * 4)) = u32x2{w0[2], w0[3]};
-      *(u32x2*)(s_dst + tile_off<kBMq>(krow, 2 * 8 + hh * 4)) = u32x2{w1[0], w1[1]};
-      *(u32x2*)(s_dst + tile_off<kBMq>(krow, 3 * 8 + hh * 4)) = u32x2{w1[2], w1[3]};
+      __bf16* row = s_dst + krow * PST + hh * 4;
+      *(u32x2*)(row + 0) = u32x2{w0[0], w0[1]};
+      *(u32x2*)(row + 8) = u32x2{w0[2], w0[3]};
+      *(u32x2*)(row + 16) = u32x2{w1[0], w1[1]};
+      *(u32x2*)(row + 24) = u32x2{w1[2], w1[3]};
     }
     __syncthreads();
 
@@ -276,9 +282,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const int k0 = (dq_k0 + ks) * 16 + hh * 8 + src_row;
-        const bf16x8 dsa = cat(tr_read<kBMq>(s_dst, k0, src_col), tr_read<kBMq>(s_dst, k0 + 4, src_col));
-        const int col = dq_blk * 32 + src_col;
-        const bf16x8 kbv = cat(tr_read<D>(s_k, k0, col), tr_read<D>(s_k, k0 + 4, col));
+        const __bf16* pd = s_dst + k0 * PST + src_col;
+        const __bf16* pk = s_k + k0 * PS + dq_blk * 32 + src_col;
+        const bf16x8 dsa = cat(tr_read(pd), tr_read(pd + 4 * PST));
+        const bf16x8 kbv = cat(tr_read(pk), tr_read(pk + 4 * PS));
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsa, kbv, acc, 0, 0, 0);
       }
       // Rows past the chunk end fall outside the resource and are dropped.
@@ -293,14 +300,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
     }
   };
 
+  // Pins the dK^T / dV^T accumulators to the accumulation registers at the step
+  // boundaries, so both unrolled steps keep them in the same place.
+  auto pin = [&]() {
+#pragma unroll
+    for (int n = 0; n < NDB; ++n) asm volatile("" : "+a"(dk_t[n]), "+a"(dv_t[n]));
+  };
+
   if (n_iter > 0) {
-    dma_rows<kBN, D>(kr_, kv_row, u0, s_k, wave, lane);  // B operand of dQ = dS K
+    // The workgroup's K and V tiles: B operands of S = Q K^T, dP = dO V^T (row
+    // reads) and of dQ = dS K (transpose reads).
+    dma_rows<kBN, D>(kr_, kv_row, u0, s_k, wave, lane);
+    dma_rows<kBN, D>(vr_, kv_row, u0, s_v, wave, lane);
     dma_q(0, q0, do0, ls0, dl0);
   }
   for (int it = 0; it < n_iter; it += 2) {
+    pin();
     step(it, q0, do0, ls0, dl0, q1, do1, ls1, dl1);
+    pin();
     if (it + 1 < n_iter) step(it + 1, q1, do1, ls1, dl1, q0, do0, ls0, dl0);
   }
+  pin();
 
   // dK, dV of this lane's key: accumulator rows are head-dim indices
   // d = n*32 + (i/4)*8 + hh*4 + i%4.

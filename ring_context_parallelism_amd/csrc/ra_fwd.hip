@@ -152,13 +152,15 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 
 template <int D>
 struct Bf16Tile {
-  static constexpr int KCH = D / 8;                    // 16-byte chunks per row
-  static constexpr int KSW = (KCH < 8 ? KCH : 8) - 1;  // K swizzle mask (b128 reads)
+  static constexpr int KCH = D / 8;                 // 16-byte chunks per row
+  static constexpr int RPW = 256 / (D * 2);         // rows per 256-byte bank window
 };
 
-// K tile: chunk c of key row r lives at chunk c ^ (r & KSW).
+// K tile: LDS serves 16 lanes x 16 bytes per clock from 64 four-byte banks, and the
+// 16-byte K reads of one clock cover 16 consecutive rows at one chunk; XOR-ing the
+// chunk with the row's window index spreads those rows over all 16 bank groups.
 template <int D>
-__device__ inline int k_swz(int r) { return r & Bf16Tile<D>::KSW; }
+__device__ inline int k_swz(int r) { return (r / Bf16Tile<D>::RPW) & (Bf16Tile<D>::KCH - 1); }
 // V tile: transpose reads touch 4 consecutive rows x 32 bytes; spread those rows
 // over distinct banks.
 template <int D>
