@@ -3,7 +3,8 @@
 One step = one pass of the whole hot path for one rank's share: the forward ring
 (ra_ring_fwd: every ring step's tiled online softmax with the fused LSE merge,
 final output rounded to bf16, LSE saved), then the backward (ra_bwd_delta, then
-ra_block_attn_bwd for every live ring step, recomputing P from the saved LSE).
+for every live ring step the dK/dV kernel and the dQ kernel, recomputing P from
+the saved LSE).
 Default workload: 16 heads x d 128, S = 131072 in the zigzag layout over p = 2,
 rank 0, bf16 -- the only workload that exercises every step, forward and backward.
 
@@ -14,9 +15,11 @@ the stream the kernels are launched on.  Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
-import math
 import os
+import re
 import sys
 import time
 
@@ -27,6 +30,16 @@ if ROOT not in sys.path:
 BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 F32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix
 HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "ring_context_parallelism_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_PROBE_BYTES = 1 << 30
+# kernel key -> (substring of the device function's name, sources it is built from)
+KERNELS = {
+    "fwd_kernel": ("fwd_bf16_kernel", ("ra_fwd.hip", "ra_internal.h")),
+    "fwd_kernel_f32": ("fwd_f32_kernel", ("ra_fwd.hip", "ra_internal.h")),
+    "bwd_dkdv_kernel": ("bwd_dkdv_kernel", ("ra_bwd.hip", "ra_internal.h")),
+    "bwd_dq_kernel": ("bwd_dq_kernel", ("ra_bwd.hip", "ra_internal.h")),
+}
 
 
 def parse():
@@ -39,7 +52,92 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run one device-to-device copy of BYTES (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
+    ap.add_argument("--pmc-summary", metavar="DIR", default=None,
+                    help="print the markdown traffic summary of the rocprofv3 --pmc runs under "
+                         "DIR (pmc_fetch/, pmc_write/, pmc_copy_fetch/, pmc_copy_write/) and exit")
     return ap.parse_args()
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_kib(run_dir, counter):
+    """Mean counter value (KiB) per dispatch, keyed by kernel name, from a --pmc run."""
+    acc = {}
+    with open(os.path.join(run_dir, "run_counter_collection.csv")) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def pmc_summary(root, workload):
+    """Traffic per dispatch from FETCH_SIZE and WRITE_SIZE, each scaled by what the same
+    counter reads for a plain device copy of COPY_PROBE_BYTES."""
+    fetch = _counter_kib(os.path.join(root, "pmc_fetch"), "FETCH_SIZE")
+    write = _counter_kib(os.path.join(root, "pmc_write"), "WRITE_SIZE")
+    cf = _counter_kib(os.path.join(root, "pmc_copy_fetch"), "FETCH_SIZE")
+    cw = _counter_kib(os.path.join(root, "pmc_copy_write"), "WRITE_SIZE")
+    copy_name = next(k for k in cf if "copyBuffer" in k)
+    f_factor = COPY_PROBE_BYTES / (cf[copy_name][0] * 1024.0)
+    w_factor = COPY_PROBE_BYTES / (cw[copy_name][0] * 1024.0)
+    cmd = ("cd /tmp && timeout -s KILL 240 rocprofv3 --pmc {c} --output-format csv -d <out>/{d} "
+           "-o run -- python3 <repo>/bench.py {a}")
+    lines = [f"# HBM traffic per dispatch: {workload} workload", "",
+             "Commands (one counter per run, on one MI355X):", "", "```"]
+    for c, d, a in (("FETCH_SIZE", "pmc_fetch", f"--workload {workload} --steps 1 --warmup 0 "
+                     "--no-cpu-baseline"),
+                    ("WRITE_SIZE", "pmc_write", f"--workload {workload} --steps 1 --warmup 0 "
+                     "--no-cpu-baseline"),
+                    ("FETCH_SIZE", "pmc_copy_fetch", f"--copy-probe {COPY_PROBE_BYTES}"),
+                    ("WRITE_SIZE", "pmc_copy_write", f"--copy-probe {COPY_PROBE_BYTES}")):
+        lines.append(cmd.format(c=c, d=d, a=a))
+    lines += ["python3 <repo>/bench.py --pmc-summary <out>", "```", "",
+              f"Calibration: a {COPY_PROBE_BYTES} B device copy (`{copy_name}`) reads "
+              f"FETCH_SIZE = {cf[copy_name][0]:.0f} KiB and WRITE_SIZE = {cw[copy_name][0]:.0f} KiB, "
+              f"so bytes = FETCH_SIZE x 1024 x {f_factor:.3f} and WRITE_SIZE x 1024 x {w_factor:.3f}.",
+              "", "| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | fetched (GB) | "
+              "written (GB) | traffic (GB) |", "|---|---|---|---|---|---|---|"]
+    data = {"workload": workload, "fetch_factor": f_factor, "write_factor": w_factor, "kernels": {}}
+    for key, (sub, files) in KERNELS.items():
+        name = next((k for k in fetch if sub in k), None)
+        if name is None or name not in write:
+            continue
+        fb = fetch[name][0] * 1024.0 * f_factor
+        wb = write[name][0] * 1024.0 * w_factor
+        data["kernels"][key] = {"name": name, "source_hash": source_hash(files),
+                                "fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb}
+        lines.append(f"| `{name[:80]}` | {fetch[name][1]} | {fetch[name][0]:.0f} | "
+                     f"{write[name][0]:.0f} | {fb / 1e9:.3f} | {wb / 1e9:.3f} | "
+                     f"{(fb + wb) / 1e9:.3f} |")
+    lines += ["", "Source hashes (sha256 prefix of the kernel's source files) identify the kernel "
+              "build the counters were taken on; `bench.py` reports `traffic` only while they "
+              "match.", "", "```json", json.dumps(data, indent=1), "```", ""]
+    return "\n".join(lines)
+
+
+def measured_traffic(workload, key):
+    """Bytes per dispatch from the committed counter summary, or None when there is none for
+    this workload or the kernel's sources changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"pmc_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    data = json.loads(m.group(1))
+    k = data["kernels"].get(key)
+    if k is None or data["workload"] != workload or k["source_hash"] != source_hash(KERNELS[key][1]):
+        return None
+    return k["traffic_bytes"]
 
 
 def step_flops(w, prob, ra):
@@ -96,8 +194,24 @@ def cpu_baseline(w, arrays, target_s):
             "seconds": dt}
 
 
+def copy_probe(nbytes):
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes}), flush=True)
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        print(pmc_summary(args.pmc_summary, args.workload))
+        return
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU ring exchange is a design note, not part of this path).",
@@ -134,7 +248,7 @@ def main():
                for _ in range(w.world)]
         dvs = [torch.empty_like(dks[0]) for _ in range(w.world)]
 
-    n_ev = 2 + (1 + len(steps) if w.backward else 0)
+    n_ev = 2 + (1 + 2 * len(steps) if w.backward else 0)
 
     def one_step(ev):
         ev[0].record(stream)
@@ -151,9 +265,12 @@ def main():
         ev[2].record(stream)
         for i, st in enumerate(steps):
             c = st["chunk"]
-            ra.ra_block_attn_bwd(prob, share.q, w.rank, share.k_chunks[c], share.v_chunks[c], c,
-                                 share.do, lse, delta, dq, dks[c], dvs[c], stream=stream)
-            ev[3 + i].record(stream)
+            args_ = (prob, share.q, w.rank, share.k_chunks[c], share.v_chunks[c], c, share.do, lse,
+                     delta)
+            ra.ra_block_attn_bwd_dkdv(*args_, dks[c], dvs[c], stream=stream)
+            ev[3 + 2 * i].record(stream)
+            ra.ra_block_attn_bwd_dq(*args_, dq, stream=stream)
+            ev[4 + 2 * i].record(stream)
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
               for _ in range(args.steps)]
@@ -185,8 +302,11 @@ def main():
                  fwd_ms_est=fwd_step_ms,
                  fwd_tflops=st["fwd_flop"] / (fwd_step_ms * 1e-3) / 1e12)
         if w.backward:
-            bms = np.array([e[2 + i].elapsed_time(e[3 + i]) for e in events])
+            kv_ms = np.array([e[2 + 2 * i].elapsed_time(e[3 + 2 * i]) for e in events])
+            q_ms = np.array([e[3 + 2 * i].elapsed_time(e[4 + 2 * i]) for e in events])
+            bms = kv_ms + q_ms
             d.update(bwd_ms=float(np.mean(bms)), bwd_ms_min=float(np.min(bms)),
+                     bwd_dkdv_ms=float(np.mean(kv_ms)), bwd_dq_ms=float(np.mean(q_ms)),
                      bwd_tflops=st["bwd_flop"] / (float(np.mean(bms)) * 1e-3) / 1e12)
         d["fwd_pct_peak"] = 100.0 * d["fwd_tflops"] / peak
         if w.backward:
@@ -216,17 +336,30 @@ def main():
         res["bwd"] = {"ms": round(bwd_ms_total, 4), "tflops": round(bwd_tflops, 3),
                       "pct_peak": round(100.0 * bwd_tflops / peak, 2), "flop": bwd_flop,
                       "delta_and_zero_ms": round(aux_ms, 4)}
-        # dominant kernel: the backward step kernel (one launch per live ring step)
-        per_launch_flop = bwd_flop / len(steps)
-        launch_ms = bwd_ms_total / len(steps)
-        name = "bwd_kernel"
-    else:
-        per_launch_flop = fwd_flop / len(steps)
-        launch_ms = fwd_step_ms
-        name = "fwd_kernel"
+    # Dominant kernel: the one with the largest share of the step.  Algorithmic FLOP
+    # per launch count only the contractions the method needs: forward 4d per
+    # visible pair (QK^T, PV); dK/dV kernel 8d (S, dP, dV, dK); dQ kernel 2d (dQ --
+    # its recomputation of S and dP is not counted).
+    pairs_bh = [st["visible_pairs_per_head"] * w.batch * w.heads_q for st in steps]
+    fwd_key = "fwd_kernel" if w.dtype == "bf16" else "fwd_kernel_f32"
+    kern = {fwd_key: (fwd_step_ms * len(steps), fwd_flop / len(steps), fwd_step_ms)}
+    if w.backward:
+        kv_ms = float(np.mean([sum(e[2 + 2 * i].elapsed_time(e[3 + 2 * i]) for i in range(len(steps)))
+                               for e in events]))
+        q_ms = float(np.mean([sum(e[3 + 2 * i].elapsed_time(e[4 + 2 * i]) for i in range(len(steps)))
+                              for e in events]))
+        res["bwd"]["dkdv_ms"] = round(kv_ms, 4)
+        res["bwd"]["dq_ms"] = round(q_ms, 4)
+        kern["bwd_dkdv_kernel"] = (kv_ms, 8.0 * w.head_dim * sum(pairs_bh) / len(steps),
+                                   kv_ms / len(steps))
+        kern["bwd_dq_kernel"] = (q_ms, 2.0 * w.head_dim * sum(pairs_bh) / len(steps),
+                                 q_ms / len(steps))
+    name = max(kern, key=lambda k: kern[k][0])
+    _, per_launch_flop, launch_ms = kern[name]
     achieved = per_launch_flop / (launch_ms * 1e-3) / 1e12
     res["roofline"] = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                       "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                       "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                       "traffic": measured_traffic(w.name, name),
                        "kernel": name, "avg_launch_ms": round(launch_ms, 4),
                        "flop_per_launch": per_launch_flop}
     if not args.no_cpu_baseline:

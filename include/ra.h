@@ -162,6 +162,23 @@ ra_status_t ra_block_attn_bwd(const ra_problem_t* prob, const void* q, int32_t q
                               const float* lse, const float* delta, float* dq, float* dk,
                               float* dv, hipStream_t stream);
 
+/*
+ * The two halves of ra_block_attn_bwd, for callers that schedule them apart (in a
+ * multi-device ring dQ stays with the query owner while dK and dV travel with the
+ * KV chunk).  Same arguments, layouts and accumulation semantics as
+ * ra_block_attn_bwd; ra_block_attn_bwd_dkdv accumulates dk and dv only,
+ * ra_block_attn_bwd_dq accumulates dq only.  Neither uses atomics: each output
+ * element has one writer, so results are deterministic.
+ */
+ra_status_t ra_block_attn_bwd_dkdv(const ra_problem_t* prob, const void* q, int32_t q_chunk,
+                                   const void* k, const void* v, int32_t kv_chunk,
+                                   const void* dout, const float* lse, const float* delta,
+                                   float* dk, float* dv, hipStream_t stream);
+ra_status_t ra_block_attn_bwd_dq(const ra_problem_t* prob, const void* q, int32_t q_chunk,
+                                 const void* k, const void* v, int32_t kv_chunk, const void* dout,
+                                 const float* lse, const float* delta, float* dq,
+                                 hipStream_t stream);
+
 /* Bytes of device workspace ra_ring_bwd needs (fp32 delta [B, Hq, L]). */
 ra_status_t ra_ring_bwd_workspace_size(const ra_problem_t* prob, size_t* bytes);
 

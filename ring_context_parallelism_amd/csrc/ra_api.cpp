@@ -366,10 +366,10 @@ static ra::BwdArgs bwd_args(const ra_problem_t* prob, const void* q, int cq, con
   return a;
 }
 
-ra_status_t ra_block_attn_bwd(const ra_problem_t* prob, const void* q, int32_t q_chunk,
-                              const void* k, const void* v, int32_t kv_chunk, const void* dout,
-                              const float* lse, const float* delta, float* dq, float* dk,
-                              float* dv, hipStream_t stream) {
+static ra_status_t block_bwd(const ra_problem_t* prob, const void* q, int32_t q_chunk,
+                             const void* k, const void* v, int32_t kv_chunk, const void* dout,
+                             const float* lse, const float* delta, float* dq, float* dk,
+                             float* dv, int which, hipStream_t stream) {
   RA_TRY(check_problem(prob));
   RA_TRY(bwd_supported(prob));
   RA_TRY(check_chunk(prob, q_chunk, "q_chunk"));
@@ -378,16 +378,41 @@ ra_status_t ra_block_attn_bwd(const ra_problem_t* prob, const void* q, int32_t q
   RA_TRY(check_ptr(k, "k"));
   RA_TRY(check_ptr(v, "v"));
   RA_TRY(check_ptr(dout, "dout"));
-  RA_TRY(check_ptr(dq, "dq"));
-  RA_TRY(check_ptr(dk, "dk"));
-  RA_TRY(check_ptr(dv, "dv"));
+  if (which & 2) RA_TRY(check_ptr(dq, "dq"));
+  if (which & 1) {
+    RA_TRY(check_ptr(dk, "dk"));
+    RA_TRY(check_ptr(dv, "dv"));
+  }
   if (lse == nullptr || delta == nullptr) return fail(RA_ERR_NULL, "lse or delta is NULL");
   const ra::LayoutMap m = make_map(prob);
   if (!step_live(prob, m, q_chunk, kv_chunk)) return ok();  // nothing visible: no-op
   ra::BwdArgs a = bwd_args(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dq, dk, dv);
-  hipError_t e = ra::launch_bwd(prob->dtype, (int)prob->head_dim_padded, a, stream);
+  hipError_t e = ra::launch_bwd(prob->dtype, (int)prob->head_dim_padded, a, which, stream);
   if (e != hipSuccess) return hip_fail(e, "ra_block_attn_bwd launch");
   return ok();
+}
+
+ra_status_t ra_block_attn_bwd(const ra_problem_t* prob, const void* q, int32_t q_chunk,
+                              const void* k, const void* v, int32_t kv_chunk, const void* dout,
+                              const float* lse, const float* delta, float* dq, float* dk,
+                              float* dv, hipStream_t stream) {
+  return block_bwd(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dq, dk, dv, 3, stream);
+}
+
+ra_status_t ra_block_attn_bwd_dkdv(const ra_problem_t* prob, const void* q, int32_t q_chunk,
+                                   const void* k, const void* v, int32_t kv_chunk,
+                                   const void* dout, const float* lse, const float* delta,
+                                   float* dk, float* dv, hipStream_t stream) {
+  return block_bwd(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, nullptr, dk, dv, 1,
+                   stream);
+}
+
+ra_status_t ra_block_attn_bwd_dq(const ra_problem_t* prob, const void* q, int32_t q_chunk,
+                                 const void* k, const void* v, int32_t kv_chunk, const void* dout,
+                                 const float* lse, const float* delta, float* dq,
+                                 hipStream_t stream) {
+  return block_bwd(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dq, nullptr, nullptr, 2,
+                   stream);
 }
 
 ra_status_t ra_ring_bwd_workspace_size(const ra_problem_t* prob, size_t* bytes) {
@@ -445,7 +470,7 @@ ra_status_t ra_ring_bwd(const ra_problem_t* prob, int32_t rank, const void* q,
     if (!step_live(prob, m, rank, c)) continue;
     ra::BwdArgs a = bwd_args(prob, q, rank, k_chunks[c], v_chunks[c], c, dout, lse, delta, dq,
                              dk_chunks[c], dv_chunks[c]);
-    e = ra::launch_bwd(prob->dtype, (int)D, a, stream);
+    e = ra::launch_bwd(prob->dtype, (int)D, a, 3, stream);
     if (e != hipSuccess) return hip_fail(e, "ra_ring_bwd launch");
   }
   return ok();

@@ -485,25 +485,30 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 template <int D>
-hipError_t launch(const BwdArgs& a, hipStream_t s) {
-  const int64_t nkv = (int64_t)a.B * a.Hkv * a.n_ktiles;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)nkv), dim3(kKvThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t nq = (int64_t)a.B * a.Hq * ((a.map.L + kQBM - 1) / kQBM);
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)nq), dim3(kQThreads), 0, s, a);
-  return hipGetLastError();
+hipError_t launch(const BwdArgs& a, int which, hipStream_t s) {
+  if (which & 1) {
+    const int64_t nkv = (int64_t)a.B * a.Hkv * a.n_ktiles;
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)nkv), dim3(kKvThreads), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (which & 2) {
+    const int64_t nq = (int64_t)a.B * a.Hq * ((a.map.L + kQBM - 1) / kQBM);
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)nq), dim3(kQThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace
 
 int bwd_block_n(int /*dtype*/, int /*D*/) { return kKvBN; }
 
-hipError_t launch_bwd(int dtype, int D, const BwdArgs& a, hipStream_t s) {
+hipError_t launch_bwd(int dtype, int D, const BwdArgs& a, int which, hipStream_t s) {
   if (dtype != RA_BF16) return hipErrorNotSupported;
-  if (D == 128) return launch<128>(a, s);
-  if (D == 64) return launch<64>(a, s);
-  if (D == 32) return launch<32>(a, s);
+  if (D == 128) return launch<128>(a, which, s);
+  if (D == 64) return launch<64>(a, which, s);
+  if (D == 32) return launch<32>(a, which, s);
   return hipErrorInvalidValue;
 }
 

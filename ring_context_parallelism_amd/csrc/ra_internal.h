@@ -82,14 +82,15 @@ struct BwdArgs {
   float scale_log2;             // scale * log2(e)
   const float* lse;             // final merged LSE (natural log), [B, Hq, L]
   const float* delta;           // rowsum(dO * O), [B, Hq, L]
-  float* dq;                    // [B, Hq, L, D]   (+=, atomics)
+  float* dq;                    // [B, Hq, L, D]   (+=)
   float* dk;                    // [B, Hkv, L, D]  (+=)
   float* dv;                    // [B, Hkv, L, D]  (+=)
 };
 
 // Launchers (defined in the .hip files).  Return the hipError_t of the launch.
 hipError_t launch_fwd(int dtype, int D, const FwdArgs& a, hipStream_t s);
-hipError_t launch_bwd(int dtype, int D, const BwdArgs& a, hipStream_t s);
+// which: 1 = dK/dV kernel, 2 = dQ kernel, 3 = both.
+hipError_t launch_bwd(int dtype, int D, const BwdArgs& a, int which, hipStream_t s);
 int fwd_block_m(int dtype, int D);
 int bwd_block_n(int dtype, int D);
 hipError_t launch_lse_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc,

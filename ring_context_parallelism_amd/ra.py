@@ -28,7 +28,8 @@ DTYPE_IDS = {"f32": RA_F32, "bf16": RA_BF16}
 
 EXPORTS = [
     "ra_block_attn_fwd", "ra_lse_merge", "ra_ring_workspace_size", "ra_ring_fwd",
-    "ra_bwd_delta", "ra_block_attn_bwd", "ra_ring_bwd_workspace_size", "ra_ring_bwd",
+    "ra_bwd_delta", "ra_block_attn_bwd", "ra_block_attn_bwd_dkdv", "ra_block_attn_bwd_dq",
+    "ra_ring_bwd_workspace_size", "ra_ring_bwd",
     "ra_positions", "ra_visible_pairs", "ra_status_str", "ra_last_error",
 ]
 
@@ -72,6 +73,8 @@ def lib():
             "ra_ring_fwd": [_PROB, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
             "ra_bwd_delta": [_PROB, _P, _P, _P, _P],
             "ra_block_attn_bwd": [_PROB, _P, _I32, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P],
+            "ra_block_attn_bwd_dkdv": [_PROB, _P, _I32, _P, _P, _I32, _P, _P, _P, _P, _P, _P],
+            "ra_block_attn_bwd_dq": [_PROB, _P, _I32, _P, _P, _I32, _P, _P, _P, _P, _P],
             "ra_ring_bwd_workspace_size": [_PROB, ctypes.POINTER(_SZ)],
             "ra_ring_bwd": [_PROB, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
             "ra_positions": [_PROB, _I32, ctypes.POINTER(_I64)],
@@ -178,6 +181,19 @@ def ra_block_attn_bwd(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dq, dk
     _check(lib().ra_block_attn_bwd(ctypes.byref(prob), _ptr(q), q_chunk, _ptr(k), _ptr(v),
                                    kv_chunk, _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq),
                                    _ptr(dk), _ptr(dv), _stream(stream)))
+
+
+def ra_block_attn_bwd_dkdv(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dk, dv,
+                           stream=None):
+    _check(lib().ra_block_attn_bwd_dkdv(ctypes.byref(prob), _ptr(q), q_chunk, _ptr(k), _ptr(v),
+                                        kv_chunk, _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dk),
+                                        _ptr(dv), _stream(stream)))
+
+
+def ra_block_attn_bwd_dq(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dq, stream=None):
+    _check(lib().ra_block_attn_bwd_dq(ctypes.byref(prob), _ptr(q), q_chunk, _ptr(k), _ptr(v),
+                                      kv_chunk, _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq),
+                                      _stream(stream)))
 
 
 def ra_ring_bwd_workspace_size(prob) -> int:

@@ -148,3 +148,27 @@ def test_full_size_backward_sampled_and_identities():
     say(f"full-size backward: |sum dV - sum dO|/|sum dO| = {rel_v:.2e}, "
         f"|sum dK|/|dK|_F = {rel_k:.2e}")
     assert rel_v < 1e-2 and rel_k < 2e-2
+
+
+def test_split_entry_points_match_combined():
+    """ra_block_attn_bwd_dkdv + ra_block_attn_bwd_dq equal ra_block_attn_bwd exactly
+    (no atomics anywhere: every output element has a single writer)."""
+    dev = need_gpu()
+    w = SMALL[2]
+    arrays = generate(w)
+    share = staging.stage(w, arrays, dev, rank=1)
+    out, lse = staging.ring_forward(share, w, rank=1)
+    L, D = w.chunk_len, w.head_dim_padded
+    delta = torch.empty((w.batch, w.heads_q, L), dtype=torch.float32, device=dev)
+    ra.ra_bwd_delta(share.prob, out, share.do, delta)
+    mk = lambda H: torch.zeros((w.batch, H, L, D), dtype=torch.float32, device=dev)
+    for c in range(w.world):
+        dq1, dk1, dv1 = mk(w.heads_q), mk(w.heads_kv), mk(w.heads_kv)
+        dq2, dk2, dv2 = mk(w.heads_q), mk(w.heads_kv), mk(w.heads_kv)
+        args = (share.prob, share.q, 1, share.k_chunks[c], share.v_chunks[c], c, share.do, lse,
+                delta)
+        ra.ra_block_attn_bwd(*args, dq1, dk1, dv1)
+        ra.ra_block_attn_bwd_dkdv(*args, dk2, dv2)
+        ra.ra_block_attn_bwd_dq(*args, dq2)
+        torch.cuda.synchronize()
+        assert torch.equal(dq1, dq2) and torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
