@@ -79,6 +79,15 @@ struct Pad {
   static constexpr int slots(int rows) { return ((rows * SCH + 63) / 64) * 64; }
 };
 
+// Row order for operands that are also read transposed.  A transpose read serves
+// 32 lanes per clock: 4 tile rows x 64 bytes.  The 4 rows of one read are the
+// accumulator rows m..m+3 of a 32x32 MFMA block; reading tile row rho(m) for
+// accumulator row m, with rho(4j + k) = 4k + j inside each 16-row block, spaces
+// those 4 rows 4 apart, and with an odd padded row stride they then fall in 16
+// distinct bank groups.  The 16-byte row reads of 16 consecutive accumulator
+// rows still touch 16 distinct rows (conflict free).
+__device__ inline int rho(int m) { return (m & ~15) | ((m & 3) << 2) | ((m >> 2) & 3); }
+
 // Swizzled tile (16-byte row reads only): XOR the chunk with the row's index among
 // the rows that share one 256-byte bank window, so 16 consecutive rows at one
 // logical chunk hit 16 distinct bank groups.
@@ -157,7 +166,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 s_k[kKvBN * D];
   __shared__ __attribute__((aligned(16))) __bf16 s_v[kKvBN * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
   const int kw = wave & 3, qs = wave >> 2;  // key block, query half
   const int L = a.map.L;
@@ -212,10 +222,12 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     dma_pad<kKvBQ, D, kKvThreads>(make_rsrc(qb, (uint32_t)L * q_row), q_row, t0, qn, wave, lane);
     dma_pad<kKvBQ, D, kKvThreads>(make_rsrc(ob, (uint32_t)L * o_row), o_row, t0, don, wave, lane);
     if (wave < 2) {  // rows past the chunk end read as 0: Q = dO = delta = 0 gives dS = 0
+      // slot s holds the statistic of query row (s & 32) + rho(s & 31) of the tile
       const float* src = (wave == 0 ? a.lse : a.delta) + ((int64_t)b * a.Hq + h) * L;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(src, (uint32_t)L * 4u),
                                                (lds_void_t*)(wave == 0 ? lsn : dln), 4,
-                                               (uint32_t)(t0 + lane) * 4u, 0, 0, 0);
+                                               (uint32_t)(t0 + (lane & 32) + rho(lane & 31)) * 4u,
+                                               0, 0, 0);
     }
   };
 
@@ -223,7 +235,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // rows r..r+3 at column c + j of the slot it and its group point at.
   const int src_row = (lane & 15) >> 2;
   const int src_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-  const int qrow = qs * 32 + l32;  // this lane's query row as an A-operand row
+  // This lane's query row as an A-operand row: accumulator row m of S and dP is
+  // query row qs*32 + rho(m) of the tile.
+  const int qrow = qs * 32 + rho(l32);
 
   auto step = [&](int it, const __bf16* qt, const __bf16* dot, const float* ls,
                   const float* dl, __bf16* qn, __bf16* don, float* lsn, float* dln) {
@@ -246,8 +260,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vbv, dp, 0, 0, 0);
     }
 
-    // P = exp2(S*scale_log2 - LSE*log2 e), dS = P (dP - delta); accumulator slot i
-    // holds query row qs*32 + gq*8 + hh*4 + e with i = gq*4 + e.
+    // P = exp2(S*scale_log2 - LSE*log2 e), dS = P (dP - delta); accumulator slot
+    // i = gq*4 + e is accumulator row m = gq*8 + hh*4 + e, query row qs*32 + rho(m)
+    // = qs*32 + 16*(gq/2) + 4e + 2*(gq&1) + hh, whose LSE and delta sit at LDS slot
+    // qs*32 + m.
     const int tq0 = t0 + qs * 32;
     const bool need_mask = tq0 < t_mask_hi;
     bf16x8 pb[2], dsb[2];
@@ -259,21 +275,22 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int i = gq * 4 + e;
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.scale_log2, -l4[e] * kLog2e));
-        if (need_mask && tq0 + gq * 8 + hh * 4 + e < t_min_lane) p = 0.0f;
+        if (need_mask && tq0 + 16 * (gq >> 1) + 4 * e + 2 * (gq & 1) + hh < t_min_lane) p = 0.0f;
         pb[i >> 3][i & 7] = (__bf16)p;
         dsb[i >> 3][i & 7] = (__bf16)(p * (dp[i] - d4[e]));
       }
     }
 
-    // dV^T += dO^T P, dK^T += Q^T dS: the A operands hold query rows
-    // mm*16 + {0..3, 8..11} + 4 hh of this half, read transposed.
+    // dV^T += dO^T P, dK^T += Q^T dS: the A operands hold the query rows of
+    // accumulator rows mm*16 + {0..3, 8..11} + 4 hh of this half, i.e. tile rows
+    // rho(.) = mm*16 + 4k + hh and mm*16 + 4k + 2 + hh (k = 0..3), read transposed.
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
       for (int n = 0; n < NDB; ++n) {
-        const int o = (qs * 32 + mm * 16 + hh * 4 + src_row) * PS + n * 32 + src_col;
-        const bf16x8 doa = cat(tr_read(dot + o), tr_read(dot + o + 8 * PS));
-        const bf16x8 qta = cat(tr_read(qt + o), tr_read(qt + o + 8 * PS));
+        const int o = (qs * 32 + mm * 16 + 4 * src_row + hh) * PS + n * 32 + src_col;
+        const bf16x8 doa = cat(tr_read(dot + o), tr_read(dot + o + 2 * PS));
+        const bf16x8 qta = cat(tr_read(qt + o), tr_read(qt + o + 2 * PS));
         dv_t[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doa, pb[mm], dv_t[n], 0, 0, 0);
         dk_t[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, dsb[mm], dk_t[n], 0, 0, 0);
       }
@@ -350,7 +367,8 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 v0[VEL];
   __shared__ __attribute__((aligned(16))) __bf16 v1[VEL];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
   const int L = a.map.L;
 
@@ -413,7 +431,8 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     __syncthreads();                     // every wave's; tile j-1 is free
     if (j + 1 < n_tiles) dma_kv(j + 1, kn, vn);
 
-    // S^T and dP^T for this tile: NB blocks of 32 keys x 32 queries.
+    // S^T and dP^T for this tile: NB blocks of 32 keys x 32 queries; accumulator
+    // row m of block blk is key blk*32 + rho(m) of the tile.
     f32x16 s[NB], dp[NB];
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
@@ -424,7 +443,7 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     for (int kk = 0; kk < NKB; ++kk)
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) {
-        const int r = blk * 32 + l32, col = kk * 16 + hh * 8;
+        const int r = blk * 32 + rho(l32), col = kk * 16 + hh * 8;
         const bf16x8 ka = *(const bf16x8*)(kt + r * PS + col);
         const bf16x8 va = *(const bf16x8*)(vt + xoff<D>(r, col));
         s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qr[kk], s[blk], 0, 0, 0);
@@ -442,22 +461,24 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       for (int i = 0; i < 16; ++i) {
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][i], a.scale_log2, -lse2));
         if (need_mask) {
-          const int u = u0 + blk * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+          // accumulator row m = (i/4)*8 + hh*4 + i%4, key rho(m)
+          const int u = u0 + blk * 32 + 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1) + hh;
           if (u >= kv_lim) p = 0.0f;
         }
         dsb[blk][i >> 3][i & 7] = (__bf16)(p * (dp[blk][i] - dlt));
       }
 
-    // dQ^T += K^T dS^T: the A operand of block (blk, mm) holds keys
-    // blk*32 + mm*16 + {0..3, 8..11} + 4 hh, read transposed from the K tile.
+    // dQ^T += K^T dS^T: the A operand of block (blk, mm) holds the keys of
+    // accumulator rows mm*16 + {0..3, 8..11} + 4 hh, i.e. tile rows
+    // blk*32 + mm*16 + 4k + hh and + 2 (k = 0..3), read transposed from the K tile.
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
         for (int n = 0; n < ND; ++n) {
-          const int o = (blk * 32 + mm * 16 + hh * 4 + src_row) * PS + n * 32 + src_col;
-          const bf16x8 kta = cat(tr_read(kt + o), tr_read(kt + o + 8 * PS));
+          const int o = (blk * 32 + mm * 16 + 4 * src_row + hh) * PS + n * 32 + src_col;
+          const bf16x8 kta = cat(tr_read(kt + o), tr_read(kt + o + 2 * PS));
           dq_t[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta, dsb[blk][mm], dq_t[n], 0, 0, 0);
         }
   };
