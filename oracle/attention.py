@@ -39,7 +39,14 @@ Readings taken where the pages are silent (each is listed in the design doc as well):
   sub-blocks r and 2p-1-r of size S/(2p), concatenated in ascending order;
   contiguous: rank r holds [r L, (r+1) L); inside every chunk the tokens are kept
   in ascending global order;
-* GQA grouping is consecutive: query head h reads KV head h // (Hq / Hkv).
+* GQA grouping is consecutive: query head h reads KV head h // (Hq / Hkv);
+* packed documents (ringmaster page, "Native recurrent context parallelism":
+  packed attention by global position boundaries, globally right-padded
+  batches): a batch element's sequence is cut by nondecreasing global positions
+  0 = e_0 <= e_1 <= ... <= e_n <= S into documents [e_k, e_k+1); a key is visible
+  only to queries of its own document (and, when causal, at or after it);
+  positions at or past e_n are right padding, seen by no query and seeing
+  nothing themselves (output 0, LSE -inf, no gradient).
 
 Parity pins (tests/test_oracle_pins.py) tie every function here to something other
 than itself: closed forms, special cases that reduce to a library routine
@@ -127,6 +134,37 @@ def _visible(k_pos: np.ndarray, q_pos: np.ndarray) -> np.ndarray:
     return k_pos[None, :] <= q_pos[:, None]
 
 
+def document_ids(bounds, seq_total: int) -> np.ndarray:
+    """Document index of every global position of one batch element; -1 = padding.
+
+    `bounds` are the global positions 0 = e_0 <= e_1 <= ... <= e_n <= S; position i
+    belongs to the document k with e_k <= i < e_k+1 (an empty document, e_k = e_k+1,
+    owns nothing), and positions i >= e_n are right padding.
+    """
+    e = np.asarray(bounds, dtype=np.int64)
+    S = int(seq_total)
+    if e.ndim != 1 or e.size < 2 or e[0] != 0 or np.any(np.diff(e) < 0) or e[-1] > S:
+        raise ValueError("bounds must be nondecreasing global positions from 0 to at most S")
+    doc = np.full(S, -1, dtype=np.int64)
+    for k in range(e.size - 1):
+        doc[e[k]:e[k + 1]] = k
+    return doc
+
+
+def _same_document(k_doc: np.ndarray, q_doc: np.ndarray) -> np.ndarray:
+    """[n_q, n_k]: key in the query's document; padding (-1) matches nothing."""
+    return (k_doc[None, :] == q_doc[:, None]) & (k_doc[None, :] >= 0)
+
+
+def _doc_rows(bounds, batch: int, seq_total: int):
+    """Per batch element document ids, or None for a dense (unpacked) problem."""
+    if bounds is None:
+        return None
+    if len(bounds) != batch:
+        raise ValueError("one boundary list per batch element")
+    return [document_ids(bounds[bi], seq_total) for bi in range(batch)]
+
+
 def _kv_head(h: int, heads_q: int, heads_kv: int) -> int:
     """KV head read by query head h under consecutive GQA grouping."""
     return h // (heads_q // heads_kv)
@@ -136,11 +174,13 @@ def _kv_head(h: int, heads_q: int, heads_kv: int) -> int:
 # Forward
 # ----------------------------------------------------------------------------------
 
-def attend(q, k, v, q_pos, k_pos, causal: bool, scale: float, row_block: int = 256):
+def attend(q, k, v, q_pos, k_pos, causal: bool, scale: float, row_block: int = 256,
+           q_doc=None, k_doc=None):
     """Exact attention of query rows q [n, d] over the keys k [m, d] / values v [m, dv].
 
     Implements softmax(q k^T * scale) v row by row with the row-wise normaliser, in
     fp64, over every key at once (no tiling of the key axis, no online rescaling).
+    With document ids (q_doc, k_doc) a key is visible only inside its own document.
     Returns (O [n, dv], lse [n]); a row with no visible key gets O = 0, lse = -inf.
     Rows are processed in blocks of `row_block` only to bound memory.
     """
@@ -157,6 +197,8 @@ def attend(q, k, v, q_pos, k_pos, causal: bool, scale: float, row_block: int = 2
         s = (q[a:b] @ k.T) * scale
         if causal:
             s = np.where(_visible(k_pos, q_pos[a:b]), s, -np.inf)
+        if q_doc is not None:
+            s = np.where(_same_document(np.asarray(k_doc), np.asarray(q_doc)[a:b]), s, -np.inf)
         m = s.max(axis=1) if s.shape[1] else np.full(b - a, -np.inf)
         live = np.isfinite(m)
         m0 = np.where(live, m, 0.0)
@@ -179,12 +221,13 @@ def _visible_key_limit(q_pos_block: np.ndarray, causal: bool, seq_total: int) ->
 
 
 def attention_fwd(Qg, Kg, Vg, rows, causal: bool, scale: float | None = None,
-                  row_block: int = 256, heads=None):
+                  row_block: int = 256, heads=None, bounds=None):
     """Exact attention of one rank's query rows against the whole global sequence.
 
     Qg [B, Hq, S, d], Kg / Vg [B, Hkv, S, d] in global token order; `rows` are the
     global positions of the rank's query rows (its share), in local order.
     `heads` optionally restricts the computation to those query heads (sampling).
+    `bounds` (one boundary list per batch element) packs documents; None = dense.
     Returns O [B, len(heads) or Hq, len(rows), d] and LSE [B, ..., len(rows)] in fp64.
     """
     B, Hq, S, d = Qg.shape
@@ -196,6 +239,7 @@ def attention_fwd(Qg, Kg, Vg, rows, causal: bool, scale: float | None = None,
     rows = np.asarray(rows, dtype=np.int64)
     key_pos = np.arange(S, dtype=np.int64)
     heads = list(range(Hq)) if heads is None else list(heads)
+    docs = _doc_rows(bounds, B, S)
     O = np.zeros((B, len(heads), rows.size, Vg.shape[3]), dtype=np.float64)
     LSE = np.full((B, len(heads), rows.size), -np.inf, dtype=np.float64)
     for bi in range(B):
@@ -204,29 +248,40 @@ def attention_fwd(Qg, Kg, Vg, rows, causal: bool, scale: float | None = None,
             for a in range(0, rows.size, row_block):
                 rb = rows[a:a + row_block]
                 lim = _visible_key_limit(rb, causal, S)
+                qd = kd = None
+                if docs is not None:
+                    qd, kd = docs[bi][rb], docs[bi][:lim]
                 o, l = attend(Qg[bi, h, rb], Kg[bi, g, :lim], Vg[bi, g, :lim], rb,
-                              key_pos[:lim], causal, scale, row_block)
+                              key_pos[:lim], causal, scale, row_block, qd, kd)
                 O[bi, hi, a:a + rb.size] = o
                 LSE[bi, hi, a:a + rb.size] = l
     return O, LSE
 
 
 def attention_partial(Q_rows, K_chunk, V_chunk, q_pos, k_pos, causal: bool,
-                      scale: float, heads_q: int, heads_kv: int):
+                      scale: float, heads_q: int, heads_kv: int, bounds=None,
+                      seq_total: int | None = None):
     """Per-step partial result: one rank's query rows against ONE KV chunk.
 
     Q_rows [B, Hq, n, d]; K_chunk / V_chunk [B, Hkv, m, d]; positions are global.
+    `bounds` (with `seq_total`) packs documents as in attention_fwd.
     Returns (O_s, LSE_s) in fp64, with O_s = 0 and LSE_s = -inf on rows that see no
     key of this chunk.  This is the quantity each ring step emits before merging.
     """
     B = Q_rows.shape[0]
+    docs = _doc_rows(bounds, B, seq_total) if bounds is not None else None
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    k_pos = np.asarray(k_pos, dtype=np.int64)
     O = np.zeros(Q_rows.shape[:3] + (V_chunk.shape[3],), dtype=np.float64)
     LSE = np.full(Q_rows.shape[:3], -np.inf, dtype=np.float64)
     for bi in range(B):
+        qd = kd = None
+        if docs is not None:
+            qd, kd = docs[bi][q_pos], docs[bi][k_pos]
         for h in range(heads_q):
             g = _kv_head(h, heads_q, heads_kv)
             O[bi, h], LSE[bi, h] = attend(Q_rows[bi, h], K_chunk[bi, g], V_chunk[bi, g],
-                                          q_pos, k_pos, causal, scale)
+                                          q_pos, k_pos, causal, scale, 256, qd, kd)
     return O, LSE
 
 
@@ -261,7 +316,7 @@ def lse_merge(o_a, lse_a, o_b, lse_b):
 # ----------------------------------------------------------------------------------
 
 def attention_bwd(Qg, Kg, Vg, dO_rows, rows, causal: bool, scale: float | None = None,
-                  row_block: int = 256, heads=None):
+                  row_block: int = 256, heads=None, bounds=None):
     """Analytic gradient of l = sum_{i in rows} dO_i . O_i for one rank's query rows.
 
     With P the row softmax of the scaled, masked scores S:
@@ -277,6 +332,8 @@ def attention_bwd(Qg, Kg, Vg, dO_rows, rows, causal: bool, scale: float | None =
     Returns dQ [B, Hq, n, d] (rows in local order), dK and dV [B, Hkv, S, d] in
     global order, all fp64.  `heads` optionally restricts dQ to those query heads
     (dO_rows then holds only those heads; dK and dV get only their contributions).
+    `bounds` packs documents as in attention_fwd; a row that sees no key (right
+    padding) has P = 0 and contributes nothing.
     """
     B, Hq, S, d = Qg.shape
     Hkv = Kg.shape[1]
@@ -285,6 +342,7 @@ def attention_bwd(Qg, Kg, Vg, dO_rows, rows, causal: bool, scale: float | None =
     rows = np.asarray(rows, dtype=np.int64)
     key_pos = np.arange(S, dtype=np.int64)
     heads = list(range(Hq)) if heads is None else list(heads)
+    docs = _doc_rows(bounds, B, S)
     dQ = np.zeros((B, len(heads), rows.size, d), dtype=np.float64)
     dK = np.zeros((B, Hkv, S, d), dtype=np.float64)
     dV = np.zeros((B, Hkv, S, Vg.shape[3]), dtype=np.float64)
@@ -302,9 +360,12 @@ def attention_bwd(Qg, Kg, Vg, dO_rows, rows, causal: bool, scale: float | None =
                 s = (q @ k.T) * scale
                 if causal:
                     s = np.where(_visible(key_pos[:lim], rb), s, -np.inf)
+                if docs is not None:
+                    s = np.where(_same_document(docs[bi][:lim], docs[bi][rb]), s, -np.inf)
                 m = s.max(axis=1)
-                e = np.exp(s - m[:, None])
-                P = e / e.sum(axis=1)[:, None]
+                live = np.isfinite(m)
+                e = np.exp(s - np.where(live, m, 0.0)[:, None])
+                P = np.where(live[:, None], e / np.where(live, e.sum(axis=1), 1.0)[:, None], 0.0)
                 O = P @ v
                 D = np.sum(do * O, axis=1)
                 dP = do @ v.T

@@ -26,6 +26,18 @@ Workloads (sizes from the pages' own models):
                    and bf16 (Mosaic post, "The Problem" / "The Implementation")
   zigzag_fwdbwd -- 16 heads x d 128, S 131072, p 2 zigzag, rank 0, causal, forward
                    then backward, N(0,1)*0.5 including dO, bf16
+  packed_fwdbwd -- zigzag_fwdbwd's shape with packed documents and right padding
+                   (ringmaster page, "Native recurrent context parallelism": packed
+                   attention by global position boundaries, globally right-padded
+                   batches); see ``document_bounds`` for the length mix
+
+Packed documents (workloads with ``docs``): a second generator,
+``default_rng([seed, 1])``, so Q/K/V/dO are the same draws as without packing.
+Per batch element: the valid length is S - floor(u * pad_frac * S) with
+u ~ U(0, 1) (the right padding); document lengths are drawn log-uniformly in
+[min_len, max_len] (rounded down to an integer) until they reach the valid length,
+the last one cut there.  The boundary lists of the batch are padded to one length
+by repeating their last entry (empty documents).
 """
 from __future__ import annotations
 
@@ -53,6 +65,7 @@ class Workload:
     value_scale: float
     backward: bool = False
     fold: tuple | None = None  # (rows, features, embed) for the tabular fold
+    docs: tuple | None = None  # (min_len, max_len, pad_frac): packed documents
 
     @property
     def chunk_len(self) -> int:
@@ -77,6 +90,9 @@ WORKLOADS = {
                              "contiguous", 0, False, "uniform", 1.0, fold=(150000, 5, 96)),
     "zigzag_fwdbwd": Workload("zigzag_fwdbwd", 4, "bf16", 1, 16, 16, 128, 128, 131072, 2,
                               "zigzag", 0, True, "normal", 0.5, backward=True),
+    "packed_fwdbwd": Workload("packed_fwdbwd", 5, "bf16", 1, 16, 16, 128, 128, 131072, 2,
+                              "zigzag", 0, True, "normal", 0.5, backward=True,
+                              docs=(256, 32768, 0.05)),
 }
 
 
@@ -121,8 +137,26 @@ def _draw(rng, shape, dist, value_scale):
     return a
 
 
+def document_bounds(w: Workload) -> np.ndarray:
+    """int32 [B, n] document boundaries (global positions) of a packed workload."""
+    min_len, max_len, pad_frac = w.docs
+    rng = np.random.default_rng([w.seed, 1])
+    S = w.seq_total
+    lists = []
+    for _ in range(w.batch):
+        valid = S - int(np.floor(rng.uniform() * pad_frac * S))
+        e = [0]
+        while e[-1] < valid:
+            n = int(np.exp(rng.uniform(np.log(min_len), np.log(max_len))))
+            e.append(min(valid, e[-1] + max(1, n)))
+        lists.append(e)
+    n = max(len(e) for e in lists)
+    return np.array([e + [e[-1]] * (n - len(e)) for e in lists], dtype=np.int32)
+
+
 def generate(w: Workload):
-    """Global-order fp32 arrays {"q", "k", "v"[, "do"]} for workload `w`.
+    """Global-order fp32 arrays {"q", "k", "v"[, "do"]} for workload `w`, plus
+    "bounds" (int32 [B, n]) for packed workloads.
 
     Values are exactly bf16 where ``w.dtype == "bf16"``.  The head dim is the true
     head dim (no padding); padding is a storage detail of the GPU side.
@@ -141,6 +175,8 @@ def generate(w: Workload):
         if w.dtype == "bf16":
             a = round_bf16(a)
         out[nm] = a
+    if w.docs is not None:
+        out["bounds"] = document_bounds(w)
     return out
 
 

@@ -14,7 +14,11 @@ Kinds of pin used (none re-types the oracle's formula against itself):
   * exact identities: shift invariance, key-permutation invariance (non-causal),
     GQA = MHA on repeated K/V, the merge identities, blockwise = unblocked for
     random chunkings, sum_j dV_j = sum_i dO_i, sum_j dK_j = 0, dQ_0 = 0;
-  * central finite differences for the backward.
+  * central finite differences for the backward;
+  * packed documents: each document equals SDPA / autograd run on that document
+    alone, Q = 0 gives LSE = ln(#visible keys of the document), values at
+    right-padding positions change nothing, and the position-to-document map
+    against a loop over its definition.
 """
 from __future__ import annotations
 
@@ -349,6 +353,175 @@ def pin_bwd_delta(impl):
     e = np.zeros_like(O)
     e[..., 2] = 1.0
     assert np.array_equal(impl.bwd_delta(e, O), O[..., 2])
+
+
+# ---------------------------------------------------------------------- packed documents
+
+# Boundary lists per batch element: documents of several lengths (one of length 1,
+# one empty), one batch element with right padding, one without.
+_PACK_S = 24
+_PACK_BOUNDS = [[0, 5, 6, 6, 15, 20], [0, 11, 24]]
+
+
+def _doc_of(bounds, i):
+    """Document index of position i by a plain scan of the boundary list; -1 = padding."""
+    for k in range(len(bounds) - 1):
+        if bounds[k] <= i < bounds[k + 1]:
+            return k
+    return -1
+
+
+def pin_document_ids_brute(impl):
+    """document_ids against a scan of the boundary definition; bad lists are rejected."""
+    for bounds, S in ((_PACK_BOUNDS[0], _PACK_S), (_PACK_BOUNDS[1], _PACK_S), ([0, 0, 3], 7),
+                      ([0, 7], 7), ([0, 0], 4)):
+        got = impl.document_ids(bounds, S)
+        assert got.tolist() == [_doc_of(bounds, i) for i in range(S)], bounds
+    for bad in ([1, 5], [0, 5, 3], [0, 30]):
+        try:
+            impl.document_ids(bad, _PACK_S)
+        except ValueError:
+            continue
+        raise AssertionError(f"accepted {bad}")
+
+
+def pin_packed_q_zero_closed_form(impl):
+    """Q = 0 with packed documents: LSE_i = ln(#visible keys of i's document) and O_i =
+    the mean of those V rows; right-padding rows get O = 0 and LSE = -inf."""
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, S, d = 2, 2, 1, _PACK_S, 3
+    Q = np.zeros((B, Hq, S, d))
+    K, V = _rand(rng, B, Hkv, S, d), _rand(rng, B, Hkv, S, d)
+    for layout, p in (("contiguous", 3), ("striped", 4), ("zigzag", 2)):
+        for causal in (True, False):
+            for r in range(p):
+                rows = impl.positions(layout, S, p, r)
+                O, LSE = impl.attention_fwd(Q, K, V, rows, causal, bounds=_PACK_BOUNDS)
+                for b in range(B):
+                    e = _PACK_BOUNDS[b]
+                    for t, i in enumerate(rows.tolist()):
+                        k = _doc_of(e, i)
+                        if k < 0:
+                            assert np.all(O[b, :, t] == 0.0) and np.all(np.isneginf(LSE[b, :, t]))
+                            continue
+                        hi = i + 1 if causal else e[k + 1]
+                        vis = list(range(e[k], hi))
+                        assert np.max(np.abs(LSE[b, :, t] - math.log(len(vis)))) < 1e-12
+                        want = V[b, 0, vis].mean(axis=0)
+                        assert np.max(np.abs(O[b, :, t] - want)) < 1e-12
+
+
+def _packed_sdpa_reference(Q, K, V, bounds, causal, scale, grad_out=None):
+    """torch SDPA (fp64) run on every document alone; right-padding rows are 0.
+    With grad_out, also the autograd gradients of sum(grad_out * O)."""
+    import torch
+    import torch.nn.functional as F
+    q, k, v = (torch.tensor(x, requires_grad=grad_out is not None) for x in (Q, K, V))
+    B, H, S, d = Q.shape
+    per_batch = []
+    for b in range(B):
+        e = bounds[b]
+        pieces = []
+        for j in range(len(e) - 1):
+            lo, hi = e[j], e[j + 1]
+            if hi > lo:
+                pieces.append(F.scaled_dot_product_attention(
+                    q[b:b + 1, :, lo:hi], k[b:b + 1, :, lo:hi], v[b:b + 1, :, lo:hi],
+                    is_causal=causal, scale=scale, enable_gqa=True))
+        pieces.append(torch.zeros((1, H, S - e[-1], d), dtype=torch.float64))
+        per_batch.append(torch.cat(pieces, dim=2))
+    out = torch.cat(per_batch, dim=0)
+    if grad_out is None:
+        return out.detach().numpy(), None
+    out.backward(torch.from_numpy(grad_out))
+    return out.detach().numpy(), (q.grad.numpy(), k.grad.numpy(), v.grad.numpy())
+
+
+def pin_packed_sdpa_per_document(impl):
+    """Packed attention of every rank's share equals torch SDPA run on each document
+    alone (fp64, GQA), with zero output on right padding."""
+    rng = np.random.default_rng(32)
+    B, Hq, Hkv, S, d = 2, 4, 2, _PACK_S, 5
+    Q, K, V = _rand(rng, B, Hq, S, d), _rand(rng, B, Hkv, S, d), _rand(rng, B, Hkv, S, d)
+    for causal in (True, False):
+        ref, _ = _packed_sdpa_reference(Q, K, V, _PACK_BOUNDS, causal, 1.0 / math.sqrt(d))
+        for layout, p in (("contiguous", 2), ("striped", 3), ("zigzag", 2)):
+            for r in range(p):
+                rows = impl.positions(layout, S, p, r)
+                O, _ = impl.attention_fwd(Q, K, V, rows, causal, bounds=_PACK_BOUNDS)
+                assert np.max(np.abs(O - ref[:, :, rows])) < 1e-12, (layout, r, causal)
+
+
+def pin_packed_bwd_autograd_per_document(impl):
+    """The packed backward equals torch autograd through per-document fp64 SDPA."""
+    rng = np.random.default_rng(33)
+    B, Hq, Hkv, S, d = 2, 4, 2, _PACK_S, 4
+    Q, K, V = _rand(rng, B, Hq, S, d), _rand(rng, B, Hkv, S, d), _rand(rng, B, Hkv, S, d)
+    for layout, causal in (("zigzag", True), ("striped", True), ("contiguous", False)):
+        for r in range(2):
+            rows = impl.positions(layout, S, 2, r)
+            dO = _rand(rng, B, Hq, rows.size, d)
+            g = np.zeros((B, Hq, S, d))
+            g[:, :, rows] = dO
+            _, (gq, gk, gv) = _packed_sdpa_reference(Q, K, V, _PACK_BOUNDS, causal,
+                                                    1.0 / math.sqrt(d), grad_out=g)
+            dQ, dK, dV = impl.attention_bwd(Q, K, V, dO, rows, causal, bounds=_PACK_BOUNDS)
+            assert np.max(np.abs(dQ - gq[:, :, rows])) < 1e-12, (layout, r)
+            assert np.max(np.abs(dK - gk)) < 1e-12, (layout, r)
+            assert np.max(np.abs(dV - gv)) < 1e-12, (layout, r)
+
+
+def pin_packed_padding_invariance(impl):
+    """Values at right-padding positions change no other output or gradient, and
+    padding rows/keys get zero output and zero gradient."""
+    rng = np.random.default_rng(34)
+    B, H, S, d = 2, 2, _PACK_S, 3
+    Q, K, V = (_rand(rng, B, H, S, d) for _ in range(3))
+    pad = [np.arange(S) >= _PACK_BOUNDS[b][-1] for b in range(B)]
+    Q2, K2, V2 = Q.copy(), K.copy(), V.copy()
+    for b in range(B):
+        for X in (Q2, K2, V2):
+            X[b, :, pad[b]] = 100.0 * _rand(rng, H, int(pad[b].sum()), d).transpose(1, 0, 2)
+    rows = impl.positions("zigzag", S, 2, 1)
+    dO = _rand(rng, B, H, rows.size, d)
+    for causal in (True, False):
+        O1, L1 = impl.attention_fwd(Q, K, V, rows, causal, bounds=_PACK_BOUNDS)
+        O2, L2 = impl.attention_fwd(Q2, K2, V2, rows, causal, bounds=_PACK_BOUNDS)
+        g1 = impl.attention_bwd(Q, K, V, dO, rows, causal, bounds=_PACK_BOUNDS)
+        g2 = impl.attention_bwd(Q2, K2, V2, dO, rows, causal, bounds=_PACK_BOUNDS)
+        assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+        for a, c in zip(g1, g2):
+            assert np.array_equal(a, c)
+        for b in range(B):
+            prow = pad[b][rows]
+            assert np.all(O1[b][:, prow] == 0.0) and np.all(np.isneginf(L1[b][:, prow]))
+            assert np.all(g1[0][b][:, prow] == 0.0)
+            assert np.all(g1[1][b][:, pad[b]] == 0.0) and np.all(g1[2][b][:, pad[b]] == 0.0)
+
+
+def pin_packed_blockwise_equals_unblocked(impl):
+    """Per-chunk partials with packed documents, LSE-merged in ring order, equal the
+    unblocked packed result."""
+    rng = np.random.default_rng(35)
+    B, Hq, Hkv, S, d = 2, 2, 1, _PACK_S, 4
+    Q, K, V = _rand(rng, B, Hq, S, d), _rand(rng, B, Hkv, S, d), _rand(rng, B, Hkv, S, d)
+    scale = 1.0 / math.sqrt(d)
+    for layout, p in (("contiguous", 3), ("zigzag", 2), ("striped", 4)):
+        for causal in (True, False):
+            r = p - 1
+            rows = impl.positions(layout, S, p, r)
+            O_ref, L_ref = impl.attention_fwd(Q, K, V, rows, causal, bounds=_PACK_BOUNDS)
+            acc_o, acc_l = None, None
+            for c in impl.ring_schedule(r, p):
+                kp = impl.positions(layout, S, p, c)
+                o, l = impl.attention_partial(Q[:, :, rows], K[:, :, kp], V[:, :, kp], rows, kp,
+                                              causal, scale, Hq, Hkv, bounds=_PACK_BOUNDS,
+                                              seq_total=S)
+                acc_o, acc_l = (o, l) if acc_o is None else impl.lse_merge(acc_o, acc_l, o, l)
+            assert np.max(np.abs(acc_o - O_ref)) < 1e-12
+            fin = np.isfinite(L_ref)
+            assert np.array_equal(fin, np.isfinite(acc_l))
+            assert np.max(np.abs(acc_l[fin] - L_ref[fin])) < 1e-12
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

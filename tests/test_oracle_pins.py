@@ -42,6 +42,15 @@ MUTATIONS = [
      "o = wb[..., None] * o_a + wa[..., None] * o_b"),
     ("merge_lse_drops_max", "hi + np.log(wa_raw + wb_raw)", "np.log(wa_raw + wb_raw)"),
     ("delta_transposed", "axis=-1)", "axis=0)"),
+    ("docs_ignored", "return (k_doc[None, :] == q_doc[:, None]) & (k_doc[None, :] >= 0)",
+     "return (k_doc[None, :] >= 0) & (q_doc[:, None] >= 0)"),
+    ("padding_keys_visible", "return (k_doc[None, :] == q_doc[:, None]) & (k_doc[None, :] >= 0)",
+     "return k_doc[None, :] == q_doc[:, None]"),
+    ("doc_boundary_off_by_one", "doc[e[k]:e[k + 1]] = k", "doc[e[k]:e[k + 1] + 1] = k"),
+    ("padding_in_first_doc", "doc = np.full(S, -1, dtype=np.int64)", "doc = np.full(S, 0, dtype=np.int64)"),
+    ("bwd_ignores_docs",
+     "s = np.where(_same_document(docs[bi][:lim], docs[bi][rb]), s, -np.inf)", "s = s"),
+    ("partial_ignores_docs", "qd, kd = docs[bi][q_pos], docs[bi][k_pos]", "qd, kd = None, None"),
 ]
 
 
