@@ -140,18 +140,23 @@ def measured_traffic(workload, key):
     return k["traffic_bytes"]
 
 
-def step_flops(w, prob, ra):
-    """Algorithmic FLOP per live ring step: exact visible pairs x 4d (fwd), x 10d (bwd)."""
+def step_flops(w, prob, ra, bounds=None):
+    """Algorithmic FLOP per live ring step: exact visible pairs x 4d (fwd), x 10d (bwd).
+    Packed workloads count pairs inside documents (summed over the batch)."""
     out = []
     for s in range(w.world):
         c = (w.rank - s) % w.world
-        pairs = ra.ra_visible_pairs(prob, w.rank, c)
-        if pairs == 0:
+        if bounds is None:
+            pairs = ra.ra_visible_pairs(prob, w.rank, c)
+            per_head = pairs * w.batch
+        else:
+            per_head = ra.ra_visible_pairs_packed(prob, w.rank, c, bounds)
+            pairs = per_head / w.batch
+        if per_head == 0:
             continue
-        bh = w.batch * w.heads_q
         out.append(dict(step=s, chunk=c, visible_pairs_per_head=pairs,
-                        fwd_flop=4.0 * w.head_dim * pairs * bh,
-                        bwd_flop=10.0 * w.head_dim * pairs * bh))
+                        fwd_flop=4.0 * w.head_dim * per_head * w.heads_q,
+                        bwd_flop=10.0 * w.head_dim * per_head * w.heads_q))
     return out
 
 
@@ -167,6 +172,7 @@ def cpu_baseline(w, arrays, target_s):
     except Exception:  # pragma: no cover - reporting only
         threads, blas = 1, "unknown"
     rows_all = oracle.positions(w.layout, w.seq_total, w.world, w.rank)
+    bounds = None if arrays.get("bounds") is None else [list(map(int, e)) for e in arrays["bounds"]]
     rng = np.random.default_rng(1234)
     n = 64
     while True:
@@ -176,14 +182,26 @@ def cpu_baseline(w, arrays, target_s):
         if w.backward:
             dO = arrays["do"][:, :1][:, :, rows]
             oracle.attention_bwd(arrays["q"], arrays["k"], arrays["v"], dO, rows, w.causal,
-                                 heads=[0])
-        oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal, heads=[0])
+                                 heads=[0], bounds=bounds)
+        oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal, heads=[0],
+                             bounds=bounds)
         dt = time.perf_counter() - t0
         if dt >= 0.6 * target_s or n >= rows_all.size:
             break
         # grow the sample towards the target wall time (at most 16x per round)
         n = int(min(rows_all.size, n * min(16.0, max(2.0, target_s / max(dt, 1e-3)))))
-    pairs = float(np.sum(rows + 1)) if w.causal else float(rows.size * w.seq_total)
+    if bounds is None:
+        pairs = float(np.sum(rows + 1)) if w.causal else float(rows.size * w.seq_total)
+    else:  # keys of the row's own document (at or before it when causal), per batch element
+        pairs = 0.0
+        for e in bounds:
+            e = np.asarray(e, dtype=np.int64)
+            k = np.searchsorted(e, rows, side="right") - 1
+            live = rows < e[-1]
+            start, end = e[np.clip(k, 0, e.size - 1)], e[np.clip(k + 1, 0, e.size - 1)]
+            cnt = np.where(w.causal, rows - start + 1, end - start)
+            pairs += float(np.sum(np.where(live, cnt, 0)))
+        pairs /= w.batch
     per_pair = (4.0 + (10.0 if w.backward else 0.0)) * w.head_dim
     flop = pairs * per_pair * w.batch
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
@@ -233,7 +251,7 @@ def main():
     arrays = generate(w)
     share = staging.stage(w, arrays, dev)
     prob = share.prob
-    steps = step_flops(w, prob, ra)
+    steps = step_flops(w, prob, ra, arrays.get("bounds"))
     L, D = w.chunk_len, w.head_dim_padded
     stream = torch.cuda.current_stream()
     tdt = staging.torch_dtype(w)

@@ -31,6 +31,18 @@
  *    Friends", "Striped Attention").  With causal != 0, key u of chunk k is
  *    visible to query t of chunk q iff pos(k, u) <= pos(q, t) (autoregressive,
  *    diagonal included).
+ *  * Packed documents (optional; ringmaster page, "Native recurrent context
+ *    parallelism": packed attention by global position boundaries, globally
+ *    right-padded batches).  seg_bounds is a DEVICE array int32 [B, seg_count]
+ *    of global positions 0 = e_0 <= e_1 <= ... <= e_{n-1} <= S per batch
+ *    element (n = seg_count >= 2); document j is [e_j, e_{j+1}) (empty when
+ *    equal; pad a shorter list by repeating its last entry).  A key is then
+ *    visible only to queries of its own document (and causal as above).
+ *    Positions >= e_{n-1} are right padding: no query sees them and they see no
+ *    key (their output is 0, their lse -inf, they get no gradient).  The
+ *    library cannot inspect device memory: a list that breaks these rules
+ *    gives unspecified values but never an access outside the caller's
+ *    buffers.  seg_bounds = NULL and seg_count = 0 mean one dense sequence.
  *  * Ownership.  The caller owns every buffer and the stream.  The library
  *    allocates nothing, keeps no pointer after returning, and holds no per-call
  *    state; calls on distinct streams are independent.
@@ -89,10 +101,11 @@ typedef struct ra_problem_t {
   int32_t causal;          /* 0 or 1 */
   int32_t dtype;           /* ra_dtype_t of q, k, v, out, dout */
   float scale;             /* 0 -> 1/sqrt(head_dim) */
-  int32_t reserved;        /* must be 0 */
+  int32_t seg_count;       /* boundaries per batch element (>= 2), or 0: dense */
   int64_t q_stride[3];     /* (b, h, t) element strides of q */
   int64_t kv_stride[3];    /* (b, h, t) element strides of every k and v chunk */
   int64_t o_stride[3];     /* (b, h, t) element strides of out and dout */
+  const int32_t* seg_bounds; /* device int32 [B, seg_count] document boundaries, or NULL */
 } ra_problem_t;
 
 /*
@@ -201,9 +214,21 @@ ra_status_t ra_positions(const ra_problem_t* prob, int32_t chunk, int64_t* host_
 /*
  * Host only.  Exact number of visible (query, key) pairs per (batch, query head)
  * between query chunk q_chunk and KV chunk kv_chunk (L*L when not causal).
+ * Dense problems only (seg_bounds == NULL): use ra_visible_pairs_packed otherwise.
  */
 ra_status_t ra_visible_pairs(const ra_problem_t* prob, int32_t q_chunk, int32_t kv_chunk,
                              int64_t* pairs);
+
+/*
+ * Host only.  Exact number of visible (query, key) pairs per query head, summed
+ * over the batch, between query chunk q_chunk and KV chunk kv_chunk of a packed
+ * problem.  host_bounds: a HOST copy of the int32 [B, prob->seg_count] boundary
+ * lists (prob->seg_bounds itself is not read); each list is validated
+ * (starts at 0, nondecreasing, ends <= S: RA_ERR_SHAPE otherwise).
+ */
+ra_status_t ra_visible_pairs_packed(const ra_problem_t* prob, int32_t q_chunk,
+                                    int32_t kv_chunk, const int32_t* host_bounds,
+                                    int64_t* pairs);
 
 /* Static string naming a status. */
 const char* ra_status_str(ra_status_t status);

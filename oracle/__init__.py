@@ -4,7 +4,9 @@ Only tests/, the smoke check and the benchmark's CPU-baseline leg may import thi
 package; the product path never does.
 """
 from .attention import (LAYOUTS, attend, attention_bwd, attention_fwd, attention_partial,
-                        bwd_delta, chunk_of_token, lse_merge, positions, ring_schedule)
+                        bwd_delta, chunk_of_token, document_ids, lse_merge, positions,
+                        ring_schedule)
 
 __all__ = ["LAYOUTS", "attend", "attention_bwd", "attention_fwd", "attention_partial",
-           "bwd_delta", "chunk_of_token", "lse_merge", "positions", "ring_schedule"]
+           "bwd_delta", "chunk_of_token", "document_ids", "lse_merge", "positions",
+           "ring_schedule"]

@@ -54,7 +54,12 @@ ra_status_t check_problem(const ra_problem_t* p) {
   if (p->causal != 0 && p->causal != 1) return fail(RA_ERR_SHAPE, "causal must be 0 or 1");
   if (p->dtype != RA_F32 && p->dtype != RA_BF16)
     return fail(RA_ERR_UNSUPPORTED, "unknown dtype %d", p->dtype);
-  if (p->reserved != 0) return fail(RA_ERR_SHAPE, "reserved must be 0");
+  if (p->seg_count < 0 || p->seg_count == 1 || p->seg_count > (1 << 24))
+    return fail(RA_ERR_SHAPE, "seg_count must be 0 (dense) or in [2, 2^24]");
+  if ((p->seg_bounds == nullptr) != (p->seg_count == 0))
+    return fail(RA_ERR_SHAPE, "seg_bounds and seg_count must be both set or both zero");
+  if (((uintptr_t)p->seg_bounds & 3u) != 0)
+    return fail(RA_ERR_SHAPE, "seg_bounds must be 4-byte aligned");
   if (!(p->scale >= 0.0f) || isinf(p->scale))
     return fail(RA_ERR_SHAPE, "scale must be finite and >= 0");
   if (p->seq_total < 1 || p->seq_total >= (int64_t(1) << 31))
@@ -149,6 +154,8 @@ ra::FwdArgs fwd_args(const ra_problem_t* p, const void* q, int cq, const void* k
   const int bm = ra::fwd_block_m(p->dtype, (int)p->head_dim_padded);
   a.n_qtiles = (a.map.L + bm - 1) / bm;
   a.scale_log2 = softmax_scale(p) * 1.4426950408889634f;
+  a.seg = p->seg_bounds;
+  a.seg_n = p->seg_count;
   return a;
 }
 
@@ -204,6 +211,8 @@ ra_status_t ra_visible_pairs(const ra_problem_t* prob, int32_t q_chunk, int32_t 
   RA_TRY(check_chunk(prob, q_chunk, "q_chunk"));
   RA_TRY(check_chunk(prob, kv_chunk, "kv_chunk"));
   if (pairs == nullptr) return fail(RA_ERR_NULL, "pairs is NULL");
+  if (prob->seg_bounds != nullptr)
+    return fail(RA_ERR_UNSUPPORTED, "packed problem: use ra_visible_pairs_packed");
   const ra::LayoutMap m = make_map(prob);
   int64_t n = 0;
   if (!prob->causal) {
@@ -212,6 +221,35 @@ ra_status_t ra_visible_pairs(const ra_problem_t* prob, int32_t q_chunk, int32_t 
     for (int32_t t = 0; t < m.L; ++t) n += ra::count_le(m, kv_chunk, ra::pos_of(m, q_chunk, t));
   }
   *pairs = n;
+  return ok();
+}
+
+ra_status_t ra_visible_pairs_packed(const ra_problem_t* prob, int32_t q_chunk,
+                                    int32_t kv_chunk, const int32_t* host_bounds,
+                                    int64_t* pairs) {
+  RA_TRY(check_problem(prob));
+  RA_TRY(check_chunk(prob, q_chunk, "q_chunk"));
+  RA_TRY(check_chunk(prob, kv_chunk, "kv_chunk"));
+  if (pairs == nullptr || host_bounds == nullptr)
+    return fail(RA_ERR_NULL, "pairs or host_bounds is NULL");
+  if (prob->seg_count < 2) return fail(RA_ERR_SHAPE, "not a packed problem (seg_count < 2)");
+  const ra::LayoutMap m = make_map(prob);
+  const int32_t n = prob->seg_count;
+  int64_t total = 0;
+  for (int64_t b = 0; b < prob->batch; ++b) {
+    const int32_t* e = host_bounds + b * n;
+    if (e[0] != 0 || e[n - 1] > m.S)
+      return fail(RA_ERR_SHAPE, "batch %lld: bounds must start at 0 and end <= S", (long long)b);
+    for (int32_t j = 1; j < n; ++j)
+      if (e[j] < e[j - 1])
+        return fail(RA_ERR_SHAPE, "batch %lld: bounds must be nondecreasing", (long long)b);
+    for (int32_t t = 0; t < m.L; ++t) {
+      int32_t lo, hi;
+      ra::key_interval(m, kv_chunk, ra::pos_of(m, q_chunk, t), prob->causal, e, n, lo, hi);
+      if (hi > lo) total += hi - lo;
+    }
+  }
+  *pairs = total;
   return ok();
 }
 
@@ -363,6 +401,8 @@ static ra::BwdArgs bwd_args(const ra_problem_t* prob, const void* q, int cq, con
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
+  a.seg = prob->seg_bounds;
+  a.seg_n = prob->seg_count;
   return a;
 }
 

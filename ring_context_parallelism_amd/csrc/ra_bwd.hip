@@ -145,7 +145,8 @@ constexpr int kKvThreads = 512;  // 8 waves
 constexpr int kKvBN = 128;       // keys per workgroup
 constexpr int kKvBQ = 64;        // query rows per iteration (two 32-row halves)
 
-template <int D>
+// PACKED: packed documents (a.seg != nullptr), a separate instantiation.
+template <int D, bool PACKED>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NKB = D / 16;  // 16-wide head-dim blocks (S and dP contractions)
   constexpr int NDB = D / 32;  // 32-row head-dim blocks of dK^T, dV^T
@@ -185,19 +186,33 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const __bf16* vb = (const __bf16*)a.v + (int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh;
   const uint32_t kv_row = (uint32_t)(a.kv_st * 2);
 
-  // Visible query range.  Query t sees key u iff t >= count_le(cq, pos(ck, u) - 1).
-  int t_first = 0, t_mask_hi = 0, t_min_lane = 0;
-  const int u_last = min(u0 + kKvBN, L) - 1;
-  if (a.causal) {
-    t_first = count_le(a.map, a.cq, pos_of(a.map, a.ck, u0) - 1);
-    t_mask_hi = count_le(a.map, a.cq, pos_of(a.map, a.ck, u_last) - 1);
-    t_min_lane = key_ok ? count_le(a.map, a.cq, pos_of(a.map, a.ck, key) - 1) : L;
-  } else {
-    t_min_lane = key_ok ? 0 : L;
+  // Queries [q_lo, q_hi) of chunk cq that see this lane's key; query tiles from
+  // t_first to t_end hold those of every key, and rows in [full_lo, full_hi) see
+  // every key of the workgroup (no mask).
+  int q_lo = 0, q_hi = L, t_first = 0, t_end = L, full_lo = 0, full_hi = L;
+  if constexpr (PACKED) {  // packed documents
+    __shared__ int red[4];
+    if (key_ok) {
+      query_interval(a.map, a.cq, pos_of(a.map, a.ck, key), a.causal,
+                     a.seg + (int64_t)b * a.seg_n, a.seg_n, q_lo, q_hi);
+    } else {
+      q_lo = L;
+      q_hi = 0;
+    }
+    wg_interval_reduce(red, q_lo, q_hi, L, t_first, t_end, full_lo, full_hi);
+  } else {  // dense: query t sees key u iff t >= count_le(cq, pos(ck, u) - 1)
+    const int u_last = min(u0 + kKvBN, L) - 1;
+    if (a.causal) {
+      t_first = count_le(a.map, a.cq, pos_of(a.map, a.ck, u0) - 1);
+      full_lo = count_le(a.map, a.cq, pos_of(a.map, a.ck, u_last) - 1);
+      q_lo = key_ok ? count_le(a.map, a.cq, pos_of(a.map, a.ck, key) - 1) : L;
+    } else {
+      q_lo = key_ok ? 0 : L;
+    }
+    if (u0 + kKvBN > L) full_lo = L;  // ragged key tile: always mask
   }
-  if (u0 + kKvBN > L) t_mask_hi = L;  // ragged key tile: always mask
   const int qt_first = t_first / kKvBQ;
-  const int n_qt = (L + kKvBQ - 1) / kKvBQ;
+  const int n_qt = (t_end + kKvBQ - 1) / kKvBQ;
   const int per_head = n_qt - qt_first;
   const int n_iter = per_head > 0 ? per_head * a.group : 0;
   if (n_iter == 0) return;  // no query of this chunk sees these keys
@@ -265,7 +280,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     // = qs*32 + 16*(gq/2) + 4e + 2*(gq&1) + hh, whose LSE and delta sit at LDS slot
     // qs*32 + m.
     const int tq0 = t0 + qs * 32;
-    const bool need_mask = tq0 < t_mask_hi;
+    // dense problems: every query at or after q_lo sees the key (q_hi = L)
+    const bool need_mask = tq0 < full_lo || (PACKED && tq0 + 32 > full_hi);
     bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
@@ -275,7 +291,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int i = gq * 4 + e;
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.scale_log2, -l4[e] * kLog2e));
-        if (need_mask && tq0 + 16 * (gq >> 1) + 4 * e + 2 * (gq & 1) + hh < t_min_lane) p = 0.0f;
+        if (need_mask) {
+          const int t = tq0 + 16 * (gq >> 1) + 4 * e + 2 * (gq & 1) + hh;
+          if (t < q_lo || (PACKED && t >= q_hi)) p = 0.0f;
+        }
         pb[i >> 3][i & 7] = (__bf16)p;
         dsb[i >> 3][i & 7] = (__bf16)(p * (dp[i] - d4[e]));
       }
@@ -352,7 +371,7 @@ constexpr int kQThreads = 256;  // 4 waves
 constexpr int kQBM = 128;       // query rows per workgroup
 constexpr int kQBN = 32;        // keys per KV tile
 
-template <int D>
+template <int D, bool PACKED>
 __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int NKB = D / 16;
   constexpr int ND = D / 32;
@@ -404,10 +423,23 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const float lse2 = tq < L ? a.lse[row] * kLog2e : 0.0f;
   const float dlt = tq < L ? a.delta[row] : 0.0f;
 
-  // Visible-key prefix of this row and of the whole tile (as in the forward).
-  const int t_last = min(t0 + kQBM, L) - 1;
-  int kv_lim = L, n_keys = L, n_full = L;
-  if (a.causal) {
+  // Visible keys of this row and of the workgroup (as in the forward): key tiles
+  // j0..n_tiles-1, no mask inside [full_lo, n_full).
+  int kv_lo = 0, kv_lim = L, j0 = 0, n_keys = L, full_lo = 0, n_full = L;
+  if constexpr (PACKED) {  // packed documents
+    __shared__ int red[4];
+    if (tq < L) {
+      key_interval(a.map, a.ck, pos_of(a.map, a.cq, tq), a.causal, a.seg + (int64_t)b * a.seg_n,
+                   a.seg_n, kv_lo, kv_lim);
+    } else {
+      kv_lo = L;
+      kv_lim = 0;
+    }
+    int min_lo;
+    wg_interval_reduce(red, kv_lo, kv_lim, L, min_lo, n_keys, full_lo, n_full);
+    j0 = min_lo / kQBN;
+  } else if (a.causal) {
+    const int t_last = min(t0 + kQBM, L) - 1;
     kv_lim = count_le(a.map, a.ck, pos_of(a.map, a.cq, min(tq, L - 1)));
     n_keys = count_le(a.map, a.ck, pos_of(a.map, a.cq, t_last));
     n_full = count_le(a.map, a.ck, pos_of(a.map, a.cq, t0));
@@ -453,7 +485,7 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     // P^T = exp2(S^T*scale_log2 - LSE*log2 e) with keys past the row's visible
     // prefix masked; dS^T = P^T (dP^T - delta).
     const int u0 = j * kQBN;
-    const bool need_mask = u0 + kQBN > n_full;
+    const bool need_mask = u0 < full_lo || u0 + kQBN > n_full;
     bf16x8 dsb[NB][2];
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk)
@@ -463,7 +495,7 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         if (need_mask) {
           // accumulator row m = (i/4)*8 + hh*4 + i%4, key rho(m)
           const int u = u0 + blk * 32 + 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1) + hh;
-          if (u >= kv_lim) p = 0.0f;
+          if (u < kv_lo || u >= kv_lim) p = 0.0f;
         }
         dsb[blk][i >> 3][i & 7] = (__bf16)(p * (dp[blk][i] - dlt));
       }
@@ -483,14 +515,14 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         }
   };
 
-  if (n_tiles > 0) dma_kv(0, k0, v0);
-  for (int j = 0; j < n_tiles; j += 2) {
+  if (n_tiles > j0) dma_kv(j0, k0, v0);
+  for (int j = j0; j < n_tiles; j += 2) {
     tile(j, k0, v0, k1, v1);
     if (j + 1 < n_tiles) tile(j + 1, k1, v1, k0, v0);
   }
 
   // dQ[q][d] += scale * dQ^T[d][q]; accumulator rows are d = n*32 + (i/4)*8 + hh*4 + i%4.
-  if (tq < L && n_tiles > 0) {
+  if (tq < L && n_tiles > j0) {
     float* dqr = a.dq + row * D;
 #pragma unroll
     for (int n = 0; n < ND; ++n)
@@ -505,17 +537,17 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-template <int D>
+template <int D, bool PK>
 hipError_t launch(const BwdArgs& a, int which, hipStream_t s) {
   if (which & 1) {
     const int64_t nkv = (int64_t)a.B * a.Hkv * a.n_ktiles;
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)nkv), dim3(kKvThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, PK>), dim3((unsigned)nkv), dim3(kKvThreads), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (which & 2) {
     const int64_t nq = (int64_t)a.B * a.Hq * ((a.map.L + kQBM - 1) / kQBM);
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)nq), dim3(kQThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, PK>), dim3((unsigned)nq), dim3(kQThreads), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -527,9 +559,10 @@ int bwd_block_n(int /*dtype*/, int /*D*/) { return kKvBN; }
 
 hipError_t launch_bwd(int dtype, int D, const BwdArgs& a, int which, hipStream_t s) {
   if (dtype != RA_BF16) return hipErrorNotSupported;
-  if (D == 128) return launch<128>(a, which, s);
-  if (D == 64) return launch<64>(a, which, s);
-  if (D == 32) return launch<32>(a, which, s);
+  const bool pk = a.seg != nullptr;
+  if (D == 128) return pk ? launch<128, true>(a, which, s) : launch<128, false>(a, which, s);
+  if (D == 64) return pk ? launch<64, true>(a, which, s) : launch<64, false>(a, which, s);
+  if (D == 32) return pk ? launch<32, true>(a, which, s) : launch<32, false>(a, which, s);
   return hipErrorInvalidValue;
 }
 

@@ -196,7 +196,9 @@ __device__ inline void dma_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_
   }
 }
 
-template <int D, int BN>
+// PK: packed documents (a.seg != nullptr).  A separate instantiation, so the
+// dense kernel carries none of the packed path's registers.
+template <int D, int BN, bool PK>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int NKB = D / 16;  // 16-wide head-dim blocks of the QK^T contraction
   constexpr int ND = D / 32;   // 32-row head-dim blocks of O^T
@@ -241,10 +243,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     qr[kk] = __builtin_bit_cast(bf16x8, w);
   }
 
-  // Visible-key prefix of this row, and of the whole tile.
-  const int t_last = min(t0 + kBM, L) - 1;
-  int kv_lim = L, n_keys = L, n_full = L;
-  if (a.causal) {
+  // Visible keys [kv_lo, kv_lim) of this row; key tiles j0..n_tiles-1 hold those of
+  // every row, and [full_lo, n_full) is visible to every row (no mask).
+  int kv_lo = 0, kv_lim = L, j0 = 0, n_keys = L, full_lo = 0, n_full = L;
+  if constexpr (PK) {  // packed documents
+    __shared__ int red[4];
+    if (tq < L) {
+      key_interval(a.map, a.ck, pos_of(a.map, a.cq, tq), a.causal, a.seg + (int64_t)b * a.seg_n,
+                   a.seg_n, kv_lo, kv_lim);
+    } else {
+      kv_lo = L;
+      kv_lim = 0;
+    }
+    int min_lo;
+    wg_interval_reduce(red, kv_lo, kv_lim, L, min_lo, n_keys, full_lo, n_full);
+    j0 = min_lo / BN;
+  } else if (a.causal) {  // dense: the visible keys are a prefix, monotone in the row
+    const int t_last = min(t0 + kBM, L) - 1;
     kv_lim = count_le(a.map, a.ck, pos_of(a.map, a.cq, min(tq, L - 1)));
     n_keys = count_le(a.map, a.ck, pos_of(a.map, a.cq, t_last));
     n_full = count_le(a.map, a.ck, pos_of(a.map, a.cq, t0));
@@ -256,7 +271,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int n = 0; n < ND; ++n) o_t[n] = f32x16{};
 
-  if (n_tiles > 0) dma_tile<D, BN>(kr_, vr_, kv_row, 0, ks0, vs0, wave, lane);
+  if (n_tiles > j0) dma_tile<D, BN>(kr_, vr_, kv_row, j0 * BN, ks0, vs0, wave, lane);
 
   // Transpose-read geometry: source lane s of each 16-lane group points at key row
   // (s / 4) of a 4-row block and head-dim column 4 (s % 4) of the lane group's 16
@@ -284,15 +299,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
         s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qr[kk], s[blk], 0, 0, 0);
       }
 
-    // Mask keys beyond this row's visible prefix (causal diagonal, ragged tail).
+    // Mask keys outside this row's visible interval (causal diagonal, document
+    // edges, ragged tail).
     const int u0 = j * BN;
-    if (u0 + BN > n_full) {
+    if (u0 < full_lo || u0 + BN > n_full) {
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int u = u0 + blk * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-          if (u >= kv_lim) s[blk][i] = kNegInf;
+          if (u < kv_lo || u >= kv_lim) s[blk][i] = kNegInf;
         }
     }
 
@@ -351,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
       }
   };
 
-  for (int j = 0; j < n_tiles; j += 2) {
+  for (int j = j0; j < n_tiles; j += 2) {
     tile(j, ks0, vs0, ks1, vs1);
     if (j + 1 < n_tiles) tile(j + 1, ks1, vs1, ks0, vs0);
   }
@@ -361,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
 // ------------------------------------------------------------------------- fp32 path
 
-template <int D, int BN>
+template <int D, int BN, bool PK>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
   constexpr int DP = D + 1;            // padded LDS row (conflict-free column reads)
   constexpr int NB = BN / 32;
@@ -392,14 +408,27 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
   for (int kk = 0; kk < D / 2; ++kk) qf[kk] = tq < L ? qb[(int64_t)tq * a.q_st + kk * 2 + hh] : 0.0f;
 
-  const int t_last = min(t0 + kBM, L) - 1;
-  int kv_lim = L, n_keys = L, n_full = L;
-  if (a.causal) {
+  // Visible keys of this row and of the workgroup, as in the bf16 kernel.
+  int kv_lo = 0, kv_lim = L, j0 = 0, n_keys = L, full_lo = 0, n_full = L;
+  if constexpr (PK) {
+    __shared__ int red[4];
+    if (tq < L) {
+      key_interval(a.map, a.ck, pos_of(a.map, a.cq, tq), a.causal, a.seg + (int64_t)b * a.seg_n,
+                   a.seg_n, kv_lo, kv_lim);
+    } else {
+      kv_lo = L;
+      kv_lim = 0;
+    }
+    int min_lo;
+    wg_interval_reduce(red, kv_lo, kv_lim, L, min_lo, n_keys, full_lo, n_full);
+    j0 = min_lo / BN;
+  } else if (a.causal) {
+    const int t_last = min(t0 + kBM, L) - 1;
     kv_lim = count_le(a.map, a.ck, pos_of(a.map, a.cq, min(tq, L - 1)));
     n_keys = count_le(a.map, a.ck, pos_of(a.map, a.cq, t_last));
     n_full = count_le(a.map, a.ck, pos_of(a.map, a.cq, t0));
   }
-  const int n_tiles = (n_keys + BN - 1) / BN;
+  const int n_tiles = (n_keys + BN - 1) / BN;  // key tiles j0 .. n_tiles-1
 
   RowState st{kMInit, 0.0f};
   f32x16 o_t[ND];
@@ -436,13 +465,13 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
       }
     }
   };
-  if (n_tiles > 0) {
-    load(0);
+  if (n_tiles > j0) {
+    load(j0 * BN);
     store(0);
   }
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
+  for (int j = j0; j < n_tiles; ++j) {
+    const int buf = (j - j0) & 1;
     __syncthreads();
     if (j + 1 < n_tiles) load((j + 1) * BN);
 
@@ -458,13 +487,13 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
       s[blk] = acc;
     }
     const int u0 = j * BN;
-    if (u0 + BN > n_full) {
+    if (u0 < full_lo || u0 + BN > n_full) {
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int u = u0 + blk * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-          if (u >= kv_lim) s[blk][i] = kNegInf;
+          if (u < kv_lo || u >= kv_lim) s[blk][i] = kNegInf;
         }
     }
     float mx = s[0][0];
@@ -520,17 +549,22 @@ hipError_t launch_grid(K kernel, const FwdArgs& a, hipStream_t s) {
 
 int fwd_block_m(int /*dtype*/, int /*D*/) { return kBM; }
 
-hipError_t launch_fwd(int dtype, int D, const FwdArgs& a, hipStream_t s) {
+template <bool PK>
+hipError_t launch_fwd_t(int dtype, int D, const FwdArgs& a, hipStream_t s) {
   if (dtype == RA_BF16) {
-    if (D == 128) return launch_grid(fwd_bf16_kernel<128, 64>, a, s);
-    if (D == 64) return launch_grid(fwd_bf16_kernel<64, 64>, a, s);
-    if (D == 32) return launch_grid(fwd_bf16_kernel<32, 64>, a, s);
+    if (D == 128) return launch_grid(fwd_bf16_kernel<128, 64, PK>, a, s);
+    if (D == 64) return launch_grid(fwd_bf16_kernel<64, 64, PK>, a, s);
+    if (D == 32) return launch_grid(fwd_bf16_kernel<32, 64, PK>, a, s);
   } else {
-    if (D == 128) return launch_grid(fwd_f32_kernel<128, 32>, a, s);
-    if (D == 64) return launch_grid(fwd_f32_kernel<64, 64>, a, s);
-    if (D == 32) return launch_grid(fwd_f32_kernel<32, 64>, a, s);
+    if (D == 128) return launch_grid(fwd_f32_kernel<128, 32, PK>, a, s);
+    if (D == 64) return launch_grid(fwd_f32_kernel<64, 64, PK>, a, s);
+    if (D == 32) return launch_grid(fwd_f32_kernel<32, 64, PK>, a, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd(int dtype, int D, const FwdArgs& a, hipStream_t s) {
+  return a.seg != nullptr ? launch_fwd_t<true>(dtype, D, a, s) : launch_fwd_t<false>(dtype, D, a, s);
 }
 
 }  // namespace ra

@@ -42,6 +42,92 @@ __host__ __device__ inline int32_t count_le(const LayoutMap& m, int32_t c, int32
   return clamp_i(X - c * m.h + 1, 0, m.h) + clamp_i(X - (2 * m.p - 1 - c) * m.h + 1, 0, m.h);
 }
 
+// Document [lo, hi) of global position X in one batch element's boundary list
+// e[0..n-1] (n >= 2, nondecreasing): e[j] <= X < e[j+1].  Returns false for right
+// padding (X >= e[n-1]) and for X < e[0].  The search keeps e[a] <= X < e[b] and
+// halves b - a, so it ends after at most log2(n) steps and reads only e[0..n-1]
+// whatever the list holds.
+__host__ __device__ inline bool doc_range(const int32_t* e, int32_t n, int32_t X, int32_t& lo,
+                                          int32_t& hi) {
+  if (X < e[0] || X >= e[n - 1]) return false;
+  int32_t a = 0, b = n - 1;
+  while (b - a > 1) {
+    const int32_t m = (a + b) >> 1;
+    if (e[m] <= X) a = m; else b = m;
+  }
+  lo = e[a];
+  hi = e[b];
+  return true;
+}
+
+// Keys of chunk ck visible to the query at global position P: the local interval
+// [lo, hi) (pos is increasing in the local index, so the visible keys of one
+// document are contiguous).  e == nullptr: dense sequence.  A query in the right
+// padding sees nothing: lo = L, hi = 0.
+__host__ __device__ inline void key_interval(const LayoutMap& m, int32_t ck, int32_t P,
+                                             int32_t causal, const int32_t* e, int32_t n,
+                                             int32_t& lo, int32_t& hi) {
+  if (e == nullptr) {
+    lo = 0;
+    hi = causal ? count_le(m, ck, P) : m.L;
+    return;
+  }
+  int32_t dlo, dhi;
+  if (!doc_range(e, n, P, dlo, dhi)) {
+    lo = m.L;
+    hi = 0;
+    return;
+  }
+  lo = count_le(m, ck, dlo - 1);
+  hi = count_le(m, ck, causal ? P : dhi - 1);
+}
+
+// Queries of chunk cq that see the key at global position P: the local interval
+// [lo, hi); a key in the right padding is seen by nobody: lo = L, hi = 0.
+__host__ __device__ inline void query_interval(const LayoutMap& m, int32_t cq, int32_t P,
+                                               int32_t causal, const int32_t* e, int32_t n,
+                                               int32_t& lo, int32_t& hi) {
+  if (e == nullptr) {
+    lo = causal ? count_le(m, cq, P - 1) : 0;
+    hi = m.L;
+    return;
+  }
+  int32_t dlo, dhi;
+  if (!doc_range(e, n, P, dlo, dhi)) {
+    lo = m.L;
+    hi = 0;
+    return;
+  }
+  lo = count_le(m, cq, (causal ? P : dlo) - 1);
+  hi = count_le(m, cq, dhi - 1);
+}
+
+#if defined(__HIPCC__)
+// Workgroup-wide (min lo, max hi, max lo, min hi) of per-lane intervals [lo, hi)
+// (packed documents): tiles from min lo to max hi hold every visible pair, and
+// [max lo, min hi) is visible to every lane.  red: 4 ints of LDS.  Every thread of
+// the workgroup must call it (two barriers).
+__device__ inline void wg_interval_reduce(int* red, int lo, int hi, int n, int& min_lo,
+                                          int& max_hi, int& max_lo, int& min_hi) {
+  if (threadIdx.x == 0) {
+    red[0] = n;
+    red[1] = 0;
+    red[2] = 0;
+    red[3] = n;
+  }
+  __syncthreads();
+  atomicMin(&red[0], lo);
+  atomicMax(&red[1], hi);
+  atomicMax(&red[2], lo);
+  atomicMin(&red[3], hi);
+  __syncthreads();
+  min_lo = red[0];
+  max_hi = red[1];
+  max_lo = red[2];
+  min_hi = red[3];
+}
+#endif
+
 // Arguments of one forward ring step.
 struct FwdArgs {
   const void* q;
@@ -63,6 +149,8 @@ struct FwdArgs {
   int32_t out_f32;
   int64_t o_sb, o_sh, o_st;
   float* lse_out;               // fp32 [B, Hq, L]
+  const int32_t* seg;           // packed-document boundaries [B, seg_n], or nullptr
+  int32_t seg_n;
 };
 
 // Arguments of one backward ring step.
@@ -85,6 +173,8 @@ struct BwdArgs {
   float* dq;                    // [B, Hq, L, D]   (+=)
   float* dk;                    // [B, Hkv, L, D]  (+=)
   float* dv;                    // [B, Hkv, L, D]  (+=)
+  const int32_t* seg;           // packed-document boundaries [B, seg_n], or nullptr
+  int32_t seg_n;
 };
 
 // Launchers (defined in the .hip files).  Return the hipError_t of the launch.

@@ -30,7 +30,8 @@ EXPORTS = [
     "ra_block_attn_fwd", "ra_lse_merge", "ra_ring_workspace_size", "ra_ring_fwd",
     "ra_bwd_delta", "ra_block_attn_bwd", "ra_block_attn_bwd_dkdv", "ra_block_attn_bwd_dq",
     "ra_ring_bwd_workspace_size", "ra_ring_bwd",
-    "ra_positions", "ra_visible_pairs", "ra_status_str", "ra_last_error",
+    "ra_positions", "ra_visible_pairs", "ra_visible_pairs_packed", "ra_status_str",
+    "ra_last_error",
 ]
 
 
@@ -47,8 +48,9 @@ class Problem(ctypes.Structure):
         ("head_dim", ctypes.c_int64), ("head_dim_padded", ctypes.c_int64),
         ("seq_total", ctypes.c_int64), ("world", ctypes.c_int32), ("layout", ctypes.c_int32),
         ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
-        ("reserved", ctypes.c_int32), ("q_stride", ctypes.c_int64 * 3),
+        ("seg_count", ctypes.c_int32), ("q_stride", ctypes.c_int64 * 3),
         ("kv_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+        ("seg_bounds", ctypes.c_void_p),
     ]
 
 
@@ -79,6 +81,8 @@ def lib():
             "ra_ring_bwd": [_PROB, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
             "ra_positions": [_PROB, _I32, ctypes.POINTER(_I64)],
             "ra_visible_pairs": [_PROB, _I32, _I32, ctypes.POINTER(_I64)],
+            "ra_visible_pairs_packed": [_PROB, _I32, _I32, ctypes.POINTER(_I32),
+                                        ctypes.POINTER(_I64)],
             "ra_status_str": [_I32],
             "ra_last_error": [],
         }
@@ -126,8 +130,11 @@ def _ptr_array(items):
 
 def make_problem(*, batch, heads_q, heads_kv, head_dim, head_dim_padded, seq_total, world,
                  layout, causal, dtype, scale=0.0, q_stride=None, kv_stride=None,
-                 o_stride=None) -> Problem:
-    """Build an ra_problem_t.  Strides default to contiguous [B, H, L, D] tensors."""
+                 o_stride=None, seg_bounds=None, seg_count=None) -> Problem:
+    """Build an ra_problem_t.  Strides default to contiguous [B, H, L, D] tensors.
+
+    seg_bounds: packed-document boundaries, a device int32 tensor [B, n] (or a raw
+    device address with seg_count); None for a dense problem."""
     L = seq_total // world if world > 0 else 0
     D = head_dim_padded
     p = Problem()
@@ -138,7 +145,11 @@ def make_problem(*, batch, heads_q, heads_kv, head_dim, head_dim_padded, seq_tot
     p.causal = int(bool(causal))
     p.dtype = DTYPE_IDS[dtype] if isinstance(dtype, str) else dtype
     p.scale = scale
-    p.reserved = 0
+    if seg_bounds is None:
+        p.seg_count, p.seg_bounds = 0, None
+    else:
+        p.seg_bounds = _ptr(seg_bounds)
+        p.seg_count = seg_count if seg_count is not None else int(seg_bounds.shape[-1])
     p.q_stride[:] = q_stride or (heads_q * L * D, L * D, D)
     p.kv_stride[:] = kv_stride or (heads_kv * L * D, L * D, D)
     p.o_stride[:] = o_stride or (heads_q * L * D, L * D, D)
@@ -223,6 +234,15 @@ def ra_positions(prob, chunk) -> np.ndarray:
 def ra_visible_pairs(prob, q_chunk, kv_chunk) -> int:
     n = _I64(0)
     _check(lib().ra_visible_pairs(ctypes.byref(prob), q_chunk, kv_chunk, ctypes.byref(n)))
+    return n.value
+
+
+def ra_visible_pairs_packed(prob, q_chunk, kv_chunk, host_bounds) -> int:
+    """host_bounds: int32 [B, seg_count] boundary lists in host memory."""
+    b = np.ascontiguousarray(host_bounds, dtype=np.int32)
+    n = _I64(0)
+    _check(lib().ra_visible_pairs_packed(ctypes.byref(prob), q_chunk, kv_chunk,
+                                         b.ctypes.data_as(ctypes.POINTER(_I32)), ctypes.byref(n)))
     return n.value
 
 

@@ -3,7 +3,8 @@
 Takes the global-order host arrays of ``workloads.generate`` and builds the device
 tensors the C ABI consumes: the rank's query chunk, every KV chunk (indexed by
 chunk id), and dO for backward workloads, each [B, H, L, D] with the head dim
-zero-padded to D.  The token order inside each chunk comes from the library's own
+zero-padded to D, plus the packed-document boundaries (int32 [B, n]) of packed
+workloads.  The token order inside each chunk comes from the library's own
 position map (``ra_positions``), so the host never re-implements the layouts.
 """
 from __future__ import annotations
@@ -17,11 +18,11 @@ from . import ra
 from .workloads import Workload
 
 
-def problem_for(w: Workload, scale: float = 0.0) -> ra.Problem:
+def problem_for(w: Workload, scale: float = 0.0, seg_bounds=None) -> ra.Problem:
     return ra.make_problem(batch=w.batch, heads_q=w.heads_q, heads_kv=w.heads_kv,
                            head_dim=w.head_dim, head_dim_padded=w.head_dim_padded,
                            seq_total=w.seq_total, world=w.world, layout=w.layout,
-                           causal=w.causal, dtype=w.dtype, scale=scale)
+                           causal=w.causal, dtype=w.dtype, scale=scale, seg_bounds=seg_bounds)
 
 
 def torch_dtype(w: Workload):
@@ -44,6 +45,7 @@ class Share:
     v_chunks: list
     do: torch.Tensor | None
     rows: np.ndarray  # global positions of the rank's query rows (library map)
+    bounds: torch.Tensor | None = None  # device int32 [B, n] (kept alive with prob)
 
 
 def stage(w: Workload, arrays: dict, device="cuda", rank: int | None = None) -> Share:
@@ -58,7 +60,11 @@ def stage(w: Workload, arrays: dict, device="cuda", rank: int | None = None) -> 
         vs.append(_to_device(arrays["v"], pos, D, dt, device))
     q = _to_device(arrays["q"], rows, D, dt, device)
     do = _to_device(arrays["do"], rows, D, dt, device) if "do" in arrays else None
-    return Share(prob, q, ks, vs, do, rows)
+    bounds = None
+    if arrays.get("bounds") is not None:
+        bounds = torch.from_numpy(np.ascontiguousarray(arrays["bounds"], dtype=np.int32)).to(device)
+        prob = problem_for(w, seg_bounds=bounds)
+    return Share(prob, q, ks, vs, do, rows, bounds)
 
 
 def ring_forward(share: Share, w: Workload, rank: int | None = None, stream=None):

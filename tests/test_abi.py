@@ -71,6 +71,40 @@ def test_visible_pairs_match_brute_force(layout, causal):
             assert ra.ra_visible_pairs(p, cq, ck) == want
 
 
+_BOUNDS = {
+    # per-batch lists (padded with repeats), documents that straddle chunks, empty
+    # and length-1 documents, right padding
+    96: np.array([[0, 7, 8, 8, 40, 41, 77, 90], [0, 50, 96, 96, 96, 96, 96, 96]], np.int32),
+}
+
+
+@pytest.mark.parametrize("layout", oracle.LAYOUTS)
+@pytest.mark.parametrize("causal", [True, False])
+def test_visible_pairs_packed_match_brute_force(layout, causal):
+    S, world = 96, 4
+    bounds = _BOUNDS[S]
+    p = _prob(batch=2, seq_total=S, world=world, layout=layout, causal=causal,
+              seg_bounds=FAKE, seg_count=bounds.shape[1])
+    docs = [oracle.document_ids(bounds[b], S) for b in range(2)]
+    for cq in range(world):
+        qp = oracle.positions(layout, S, world, cq)
+        for ck in range(world):
+            kp = oracle.positions(layout, S, world, ck)
+            want = 0
+            for d in docs:
+                vis = (d[kp][None, :] == d[qp][:, None]) & (d[kp][None, :] >= 0)
+                if causal:
+                    vis &= kp[None, :] <= qp[:, None]
+                want += int(vis.sum())
+            assert ra.ra_visible_pairs_packed(p, cq, ck, bounds) == want
+    assert _status_of(ra.ra_visible_pairs, p, 0, 0) == ra.RA_ERR_UNSUPPORTED
+    for bad in ([[1, 96]] * 2, [[0, 50, 40]] * 2, [[0, 97]] * 2):
+        q = _prob(batch=2, seq_total=S, world=world, layout=layout, seg_bounds=FAKE,
+                  seg_count=len(bad[0]))
+        assert _status_of(ra.ra_visible_pairs_packed, q, 0, 0, np.array(bad, np.int32)) == \
+            ra.RA_ERR_SHAPE
+
+
 def test_workspace_sizes():
     p = _prob(batch=2, heads_q=4, seq_total=64, world=2, head_dim_padded=128, head_dim=128)
     assert ra.ra_ring_workspace_size(p) == 2 * 4 * 32 * 128 * 4
@@ -98,6 +132,9 @@ FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced on thes
     (dict(dtype=9), ra.RA_ERR_UNSUPPORTED),
     (dict(q_stride=(0, 0, 3)), ra.RA_ERR_SHAPE),
     (dict(scale=-1.0), ra.RA_ERR_SHAPE),
+    (dict(seg_bounds=FAKE, seg_count=1), ra.RA_ERR_SHAPE),
+    (dict(seg_bounds=FAKE, seg_count=0), ra.RA_ERR_SHAPE),
+    (dict(seg_bounds=FAKE + 2, seg_count=4), ra.RA_ERR_SHAPE),
 ])
 def test_problem_validation(kw, status):
     p = _prob(**kw)
