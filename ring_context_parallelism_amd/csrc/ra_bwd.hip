@@ -14,8 +14,9 @@
 //    64-row query tile.  Scores are computed as S[q][key] (every lane holds one key
 //    and 16 query rows), so P and dS feed dV^T = dO^T P and dK^T = Q^T dS straight
 //    from registers; the two partial dK^T/dV^T accumulators of a key block are
-//    summed through LDS at the end.  K and V stay in LDS; query tiles (Q, dO, LSE,
-//    delta) stream through double-buffered LDS.  Two waves per SIMD.
+//    summed through LDS at the end.  Each lane's K row stays in registers and V in
+//    LDS; query tiles (Q, dO, LSE, delta) stream through double-buffered LDS.  Two
+//    waves per SIMD.
 //
 //  * dQ kernel -- the forward's shape: one workgroup = 4 waves = 128 query rows of
 //    one (batch, query head), KV tiles of 32 keys streamed through double-buffered
@@ -164,7 +165,6 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float ls1[kKvBQ];
   __shared__ __attribute__((aligned(16))) float dl0[kKvBQ];
   __shared__ __attribute__((aligned(16))) float dl1[kKvBQ];
-  __shared__ __attribute__((aligned(16))) __bf16 s_k[kKvBN * D];
   __shared__ __attribute__((aligned(16))) __bf16 s_v[kKvBN * D];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -224,28 +224,46 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     dk_t[n] = f32x16{};
   }
 
-  auto tile_of = [&](int it, int& h, int& t0) {
-    h = g * a.group + it / per_head;
-    t0 = (qt_first + it % per_head) * kKvBQ;
-  };
-  auto dma_q = [&](int it, __bf16* qn, __bf16* don, float* lsn, float* dln) {
-    int h, t0;
-    tile_of(it, h, t0);
-    const __bf16* qb = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
-    const __bf16* ob = (const __bf16*)a.dout + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;
-    const uint32_t q_row = (uint32_t)(a.q_st * 2), o_row = (uint32_t)(a.o_st * 2);
-    dma_pad<kKvBQ, D, kKvThreads>(make_rsrc(qb, (uint32_t)L * q_row), q_row, t0, qn, wave, lane);
-    dma_pad<kKvBQ, D, kKvThreads>(make_rsrc(ob, (uint32_t)L * o_row), o_row, t0, don, wave, lane);
+  // Iterations walk the query tiles [t_lo, t_hi) of one head, then the next head of
+  // the GQA group.  The next DMA's tile (head base pointers and first row) advances
+  // incrementally, without a division per iteration.
+  const int t_lo = qt_first * kKvBQ, t_hi = n_qt * kKvBQ;
+  const uint32_t q_row = (uint32_t)(a.q_st * 2), o_row = (uint32_t)(a.o_st * 2);
+  const int h0 = g * a.group;
+  const __bf16* nq = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h0 * a.q_sh;
+  const __bf16* no = (const __bf16*)a.dout + (int64_t)b * a.o_sb + (int64_t)h0 * a.o_sh;
+  const float* nst = (wave == 0 ? a.lse : a.delta) + ((int64_t)b * a.Hq + h0) * L;
+  int nt = t_lo;   // first row of the next DMA's tile
+  int ct = t_lo;   // first row of the current step's tile
+  auto dma_q = [&](__bf16* qn, __bf16* don, float* lsn, float* dln) {
+    dma_pad<kKvBQ, D, kKvThreads>(make_rsrc(nq, (uint32_t)L * q_row), q_row, nt, qn, wave, lane);
+    dma_pad<kKvBQ, D, kKvThreads>(make_rsrc(no, (uint32_t)L * o_row), o_row, nt, don, wave, lane);
     if (wave < 2) {  // rows past the chunk end read as 0: Q = dO = delta = 0 gives dS = 0
       // slot s holds the statistic of query row (s & 32) + rho(s & 31) of the tile
-      const float* src = (wave == 0 ? a.lse : a.delta) + ((int64_t)b * a.Hq + h) * L;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(src, (uint32_t)L * 4u),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(nst, (uint32_t)L * 4u),
                                                (lds_void_t*)(wave == 0 ? lsn : dln), 4,
-                                               (uint32_t)(t0 + (lane & 32) + rho(lane & 31)) * 4u,
+                                               (uint32_t)(nt + (lane & 32) + rho(lane & 31)) * 4u,
                                                0, 0, 0);
+    }
+    nt += kKvBQ;
+    if (nt >= t_hi) {
+      nt = t_lo;
+      nq += a.q_sh;
+      no += a.o_sh;
+      nst += L;
     }
   };
 
+  // This lane's key row of K as the B operand of S = Q K^T, held in registers for
+  // the whole kernel (rows past the chunk end read as 0): the K tile is never
+  // re-read from LDS.
+  bf16x8 kreg[NKB];
+  {
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, (uint32_t)L * kv_row);
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk)
+      kreg[kk] = load_row8(kr, (uint32_t)key * kv_row + (uint32_t)(kk * 32 + hh * 16));
+  }
   // Transpose-read source slot of this lane: lane j of each 16-lane group receives
   // rows r..r+3 at column c + j of the slot it and its group point at.
   const int src_row = (lane & 15) >> 2;
@@ -256,11 +274,12 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   auto step = [&](int it, const __bf16* qt, const __bf16* dot, const float* ls,
                   const float* dl, __bf16* qn, __bf16* don, float* lsn, float* dln) {
-    int h, t0;
-    tile_of(it, h, t0);
+    const int t0 = ct;
+    ct = ct + kKvBQ >= t_hi ? t_lo : ct + kKvBQ;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile `it`
     __syncthreads();                     // every wave's; tile it-1 is free
-    if (it + 1 < n_iter) dma_q(it + 1, qn, don, lsn, dln);
+    if (it + 1 < n_iter) dma_q(qn, don, lsn, dln);
+    __builtin_amdgcn_iglp_opt(0);  // scheduling hint: interleave LDS reads with MFMAs
 
     // S[q][key], dP[q][key] for this wave's query half and 32 keys.
     f32x16 s = {}, dp = {};
@@ -269,7 +288,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const int col = kk * 16 + hh * 8;
       const bf16x8 qa = *(const bf16x8*)(qt + qrow * PS + col);
       const bf16x8 da = *(const bf16x8*)(dot + qrow * PS + col);
-      const bf16x8 kbv = *(const bf16x8*)(s_k + xoff<D>(krow, col));
+      const bf16x8 kbv = kreg[kk];
       const bf16x8 vbv = *(const bf16x8*)(s_v + xoff<D>(krow, col));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kbv, s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vbv, dp, 0, 0, 0);
@@ -303,6 +322,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     // dV^T += dO^T P, dK^T += Q^T dS: the A operands hold the query rows of
     // accumulator rows mm*16 + {0..3, 8..11} + 4 hh of this half, i.e. tile rows
     // rho(.) = mm*16 + 4k + hh and mm*16 + 4k + 2 + hh (k = 0..3), read transposed.
+    __builtin_amdgcn_s_setprio(1);  // MFMA phase first when two waves compete for issue
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
@@ -313,12 +333,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         dv_t[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doa, pb[mm], dv_t[n], 0, 0, 0);
         dk_t[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, dsb[mm], dk_t[n], 0, 0, 0);
       }
+    __builtin_amdgcn_s_setprio(0);
   };
 
-  // The workgroup's K and V tiles (B operands of S = Q K^T and dP = dO V^T).
-  dma_xor<kKvBN, D, kKvThreads>(make_rsrc(kb, (uint32_t)L * kv_row), kv_row, u0, s_k, wave, lane);
   dma_xor<kKvBN, D, kKvThreads>(make_rsrc(vb, (uint32_t)L * kv_row), kv_row, u0, s_v, wave, lane);
-  dma_q(0, q0, do0, ls0, dl0);
+  dma_q(q0, do0, ls0, dl0);
   for (int it = 0; it < n_iter; it += 2) {
     step(it, q0, do0, ls0, dl0, q1, do1, ls1, dl1);
     if (it + 1 < n_iter) step(it + 1, q1, do1, ls1, dl1, q0, do0, ls0, dl0);
