@@ -285,6 +285,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile j landed
     __syncthreads();                     // ... and every other wave's; tile j-1 is free
     if (j + 1 < n_tiles) dma_tile<D, BN>(kr_, vr_, kv_row, (j + 1) * BN, kn, vn, wave, lane);
+    __builtin_amdgcn_iglp_opt(0);  // scheduling hint: interleave LDS reads with MFMAs
 
     // S^T for this tile: NB blocks of 32 keys x 32 queries.
     f32x16 s[NB];
