@@ -301,6 +301,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int tq0 = t0 + qs * 32;
     // dense problems: every query at or after q_lo sees the key (q_hi = L)
     const bool need_mask = tq0 < full_lo || (PACKED && tq0 + 32 > full_hi);
+    // Row t = tq0 + c(gq, e) + hh with c = 16*(gq/2) + 4e + 2*(gq&1) is masked when
+    // c < lo_c or c >= hi_c; outside the masked tiles the limits admit every row, so
+    // the loop has no branch and two VALU per element for the mask.
+    const int lo_c = need_mask ? q_lo - tq0 - hh : -64;
+    const int hi_c = (PACKED && need_mask) ? q_hi - tq0 - hh : 64;
     bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
@@ -309,11 +314,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = gq * 4 + e;
+        const int c = 16 * (gq >> 1) + 4 * e + 2 * (gq & 1);
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.scale_log2, -l4[e] * kLog2e));
-        if (need_mask) {
-          const int t = tq0 + 16 * (gq >> 1) + 4 * e + 2 * (gq & 1) + hh;
-          if (t < q_lo || (PACKED && t >= q_hi)) p = 0.0f;
-        }
+        if (c < lo_c || (PACKED && c >= hi_c)) p = 0.0f;
         pb[i >> 3][i & 7] = (__bf16)p;
         dsb[i >> 3][i & 7] = (__bf16)(p * (dp[i] - d4[e]));
       }
@@ -505,19 +508,28 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     // prefix masked; dS^T = P^T (dP^T - delta).
     const int u0 = j * kQBN;
     const bool need_mask = u0 < full_lo || u0 + kQBN > n_full;
+    float pv[NB][16];
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        pv[blk][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][i], a.scale_log2, -lse2));
+    if (__builtin_expect(need_mask, 0)) {  // rare: keep it a branch
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          // accumulator row m = (i/4)*8 + hh*4 + i%4, key rho(m)
+          const int u = u0 + blk * 32 + 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1) + hh;
+          if (u < kv_lo || u >= kv_lim) pv[blk][i] = 0.0f;
+        }
+    }
     bf16x8 dsb[NB][2];
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][i], a.scale_log2, -lse2));
-        if (need_mask) {
-          // accumulator row m = (i/4)*8 + hh*4 + i%4, key rho(m)
-          const int u = u0 + blk * 32 + 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1) + hh;
-          if (u < kv_lo || u >= kv_lim) p = 0.0f;
-        }
-        dsb[blk][i >> 3][i & 7] = (__bf16)(p * (dp[blk][i] - dlt));
-      }
+      for (int i = 0; i < 16; ++i)
+        dsb[blk][i >> 3][i & 7] = (__bf16)(pv[blk][i] * (dp[blk][i] - dlt));
 
     // dQ^T += K^T dS^T: the A operand of block (blk, mm) holds the keys of
     // accumulator rows mm*16 + {0..3, 8..11} + 4 hh, i.e. tile rows
