@@ -9,14 +9,14 @@
 // Two kernels, neither of which uses atomics (every output element has exactly
 // one writer, so the result is deterministic):
 //
-//  * dK/dV kernel -- one workgroup = 8 waves = 128 keys of one (batch, KV head).
-//    Waves w and w+4 own the same 32 keys and take the two 32-row halves of each
-//    64-row query tile.  Scores are computed as S[q][key] (every lane holds one key
-//    and 16 query rows), so P and dS feed dV^T = dO^T P and dK^T = Q^T dS straight
-//    from registers; the two partial dK^T/dV^T accumulators of a key block are
-//    summed through LDS at the end.  Each lane's K row stays in registers and V in
-//    LDS; query tiles (Q, dO, LSE, delta) stream through double-buffered LDS.  Two
-//    waves per SIMD.
+//  * dK/dV kernel -- one workgroup = 4 waves = 128 keys of one (batch, KV head);
+//    each wave owns 32 keys and walks every 32-row query tile that sees them.
+//    Scores are computed as S[q][key] (every lane holds one key and 16 query rows),
+//    so P and dS feed dV^T = dO^T P and dK^T = Q^T dS straight from registers.
+//    Each lane's K row stays in registers and V in LDS; query tiles (Q, dO, LSE,
+//    delta) stream through double-buffered LDS.  Two workgroups per CU, so the two
+//    waves sharing a SIMD belong to different workgroups and their barriers do not
+//    keep them in step.
 //
 //  * dQ kernel -- the forward's shape: one workgroup = 4 waves = 128 query rows of
 //    one (batch, query head), KV tiles of 32 keys streamed through double-buffered
@@ -142,13 +142,13 @@ __device__ inline void dma_xor(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, in
 
 // ------------------------------------------------------------------ dK/dV kernel
 
-constexpr int kKvThreads = 512;  // 8 waves
+constexpr int kKvThreads = 256;  // 4 waves, each 32 keys
 constexpr int kKvBN = 128;       // keys per workgroup
-constexpr int kKvBQ = 64;        // query rows per iteration (two 32-row halves)
+constexpr int kKvBQ = 32;        // query rows per iteration
 
 // PACKED: packed documents (a.seg != nullptr), a separate instantiation.
 template <int D, bool PACKED>
-__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NKB = D / 16;  // 16-wide head-dim blocks (S and dP contractions)
   constexpr int NDB = D / 32;  // 32-row head-dim blocks of dK^T, dV^T
   using PQ = Pad<D>;
@@ -161,16 +161,17 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 q1[QEL];
   __shared__ __attribute__((aligned(16))) __bf16 do0[QEL];
   __shared__ __attribute__((aligned(16))) __bf16 do1[QEL];
-  __shared__ __attribute__((aligned(16))) float ls0[kKvBQ];
-  __shared__ __attribute__((aligned(16))) float ls1[kKvBQ];
-  __shared__ __attribute__((aligned(16))) float dl0[kKvBQ];
-  __shared__ __attribute__((aligned(16))) float dl1[kKvBQ];
+  // LSE / delta slots: one 64-lane DMA fills 64; the first kKvBQ are the tile's
+  __shared__ __attribute__((aligned(16))) float ls0[64];
+  __shared__ __attribute__((aligned(16))) float ls1[64];
+  __shared__ __attribute__((aligned(16))) float dl0[64];
+  __shared__ __attribute__((aligned(16))) float dl1[64];
   __shared__ __attribute__((aligned(16))) __bf16 s_v[kKvBN * D];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
-  const int kw = wave & 3, qs = wave >> 2;  // key block, query half
+  const int kw = wave;  // 32-key block of this wave
   const int L = a.map.L;
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -269,8 +270,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int src_row = (lane & 15) >> 2;
   const int src_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
   // This lane's query row as an A-operand row: accumulator row m of S and dP is
-  // query row qs*32 + rho(m) of the tile.
-  const int qrow = qs * 32 + rho(l32);
+  // query row rho(m) of the tile.
+  const int qrow = rho(l32);
 
   auto step = [&](int it, const __bf16* qt, const __bf16* dot, const float* ls,
                   const float* dl, __bf16* qn, __bf16* don, float* lsn, float* dln) {
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     if (it + 1 < n_iter) dma_q(qn, don, lsn, dln);
     __builtin_amdgcn_iglp_opt(0);  // scheduling hint: interleave LDS reads with MFMAs
 
-    // S[q][key], dP[q][key] for this wave's query half and 32 keys.
+    // S[q][key], dP[q][key] for the tile's 32 query rows and this wave's 32 keys.
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {
@@ -295,10 +296,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
 
     // P = exp2(S*scale_log2 - LSE*log2 e), dS = P (dP - delta); accumulator slot
-    // i = gq*4 + e is accumulator row m = gq*8 + hh*4 + e, query row qs*32 + rho(m)
-    // = qs*32 + 16*(gq/2) + 4e + 2*(gq&1) + hh, whose LSE and delta sit at LDS slot
-    // qs*32 + m.
-    const int tq0 = t0 + qs * 32;
+    // i = gq*4 + e is accumulator row m = gq*8 + hh*4 + e, query row rho(m)
+    // = 16*(gq/2) + 4e + 2*(gq&1) + hh of the tile, whose LSE and delta sit at LDS
+    // slot m.
+    const int tq0 = t0;
     // dense problems: every query at or after q_lo sees the key (q_hi = L)
     const bool need_mask = tq0 < full_lo || (PACKED && tq0 + 32 > full_hi);
     // Row t = tq0 + c(gq, e) + hh with c = 16*(gq/2) + 4e + 2*(gq&1) is masked when
@@ -309,8 +310,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      const f32x4 l4 = *(const f32x4*)(ls + qs * 32 + gq * 8 + hh * 4);
-      const f32x4 d4 = *(const f32x4*)(dl + qs * 32 + gq * 8 + hh * 4);
+      const f32x4 l4 = *(const f32x4*)(ls + gq * 8 + hh * 4);
+      const f32x4 d4 = *(const f32x4*)(dl + gq * 8 + hh * 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = gq * 4 + e;
@@ -323,14 +324,14 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
 
     // dV^T += dO^T P, dK^T += Q^T dS: the A operands hold the query rows of
-    // accumulator rows mm*16 + {0..3, 8..11} + 4 hh of this half, i.e. tile rows
+    // accumulator rows mm*16 + {0..3, 8..11} + 4 hh, i.e. tile rows
     // rho(.) = mm*16 + 4k + hh and mm*16 + 4k + 2 + hh (k = 0..3), read transposed.
     __builtin_amdgcn_s_setprio(1);  // MFMA phase first when two waves compete for issue
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
       for (int n = 0; n < NDB; ++n) {
-        const int o = (qs * 32 + mm * 16 + 4 * src_row + hh) * PS + n * 32 + src_col;
+        const int o = (mm * 16 + 4 * src_row + hh) * PS + n * 32 + src_col;
         const bf16x8 doa = cat(tr_read(dot + o), tr_read(dot + o + 2 * PS));
         const bf16x8 qta = cat(tr_read(qt + o), tr_read(qt + o + 2 * PS));
         dv_t[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doa, pb[mm], dv_t[n], 0, 0, 0);
@@ -346,44 +347,25 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     if (it + 1 < n_iter) step(it + 1, q1, do1, ls1, dl1, q0, do0, ls0, dl0);
   }
 
-  // Sum the two query halves' partial accumulators of each key block through LDS
-  // (the query-tile buffers are free now), then add into dK and dV.  Accumulator
-  // rows are head-dim indices d = n*32 + (i/4)*8 + hh*4 + i%4.
-  float* red = (float*)q0;  // 4 waves x 64 lanes x 8 floats per round
-  static_assert(4 * 64 * 8 * 4 <= QEL * 2, "reduction buffer too small");
-  const int64_t grow = (((int64_t)b * a.Hkv + g) * L + key) * D;
+  // Add into dK and dV; accumulator rows are head-dim indices
+  // d = n*32 + (i/4)*8 + hh*4 + i%4 of this lane's key.
+  if (key_ok) {
+    const int64_t grow = (((int64_t)b * a.Hkv + g) * L + key) * D;
 #pragma unroll
-  for (int n = 0; n < NDB; ++n) {
+    for (int n = 0; n < NDB; ++n)
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
+      for (int gq = 0; gq < 4; ++gq) {
+        f32x4* pk = (f32x4*)(a.dk + grow + n * 32 + gq * 8 + hh * 4);
+        f32x4* pv = (f32x4*)(a.dv + grow + n * 32 + gq * 8 + hh * 4);
+        f32x4 ck = *pk, cv = *pv;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const f32x16& mine = which == 0 ? dk_t[n] : dv_t[n];
-        __syncthreads();
-        if (qs == 1) {
-#pragma unroll
-          for (int i = 0; i < 8; i += 4)
-            *(f32x4*)(red + ((kw * 64 + lane) * 8 + i)) =
-                f32x4{mine[half * 8 + i], mine[half * 8 + i + 1], mine[half * 8 + i + 2],
-                      mine[half * 8 + i + 3]};
+        for (int e = 0; e < 4; ++e) {
+          ck[e] += dk_t[n][gq * 4 + e] * a.scale;
+          cv[e] += dv_t[n][gq * 4 + e];
         }
-        __syncthreads();
-        if (qs == 0 && key_ok) {
-          float* dst = (which == 0 ? a.dk : a.dv) + grow + n * 32;
-          const float sc = which == 0 ? a.scale : 1.0f;
-#pragma unroll
-          for (int g2 = 0; g2 < 2; ++g2) {
-            const int gq = half * 2 + g2;
-            const f32x4 o4 = *(const f32x4*)(red + ((kw * 64 + lane) * 8 + g2 * 4));
-            f32x4* p = (f32x4*)(dst + gq * 8 + hh * 4);
-            f32x4 c = *p;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) c[e] += (mine[gq * 4 + e] + o4[e]) * sc;
-            *p = c;
-          }
-        }
+        *pk = ck;
+        *pv = cv;
       }
-    }
   }
 }
 
