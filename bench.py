@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run one device-to-device copy of BYTES (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
+    ap.add_argument("--sq-summary", metavar="DIR", default=None,
+                    help="print the markdown summary of the three SQ-counter --pmc runs under "
+                         "DIR (cnt_1/, cnt_2/, cnt_3/) and exit")
     ap.add_argument("--pmc-summary", metavar="DIR", default=None,
                     help="print the markdown traffic summary of the rocprofv3 --pmc runs under "
                          "DIR (pmc_fetch/, pmc_write/, pmc_copy_fetch/, pmc_copy_write/) and exit")
@@ -121,6 +124,59 @@ def pmc_summary(root, workload):
     lines += ["", "Source hashes (sha256 prefix of the kernel's source files) identify the kernel "
               "build the counters were taken on; `bench.py` reports `traffic` only while they "
               "match.", "", "```json", json.dumps(data, indent=1), "```", ""]
+    return "\n".join(lines)
+
+
+SQ_PASSES = (
+    "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_LDS "
+    "SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS SQ_LDS_IDX_ACTIVE",
+    "SQ_LDS_BANK_CONFLICT SQ_LDS_ADDR_CONFLICT SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL "
+    "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_MISC SQ_WAIT_ANY SQ_BUSY_CU_CYCLES",
+    "SQ_INSTS_VALU SQ_ACTIVE_INST_ANY SQ_WAIT_INST_ANY SQ_INST_LEVEL_LDS SQ_INSTS_SALU "
+    "SQ_ACTIVE_INST_SCA SQ_INSTS_VMEM SQ_WAVES",
+)
+
+
+def sq_summary(root, workload, n_cu=256):
+    """Per-kernel ratios from three SQ-counter passes (one launch of each kernel per step)."""
+    agg, dur = {}, {}
+    for i in range(len(SQ_PASSES)):
+        with open(os.path.join(root, f"cnt_{i + 1}", "run_counter_collection.csv")) as fh:
+            for r in csv.DictReader(fh):
+                key = next((k for k, (sub, _) in KERNELS.items() if sub in r["Kernel_Name"]), None)
+                if key is None:
+                    continue
+                agg.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+                dur.setdefault(key, {})[(i, r["Dispatch_Id"])] = (
+                    int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    cmd = ("cd /tmp && timeout -s KILL 200 rocprofv3 --pmc {c} --output-format csv -d <out>/cnt_{i} "
+           "-o run -- python3 <repo>/bench.py --workload {w} --steps 1 --warmup 0 --no-cpu-baseline")
+    lines = [f"# SQ counters per kernel: {workload} workload", "",
+             "Commands (three passes, at most 8 SQ counters each, on one MI355X):", "", "```"]
+    lines += [cmd.format(c=c, i=i + 1, w=workload) for i, c in enumerate(SQ_PASSES)]
+    lines += ["python3 <repo>/bench.py --sq-summary <out>", "```", "",
+              "Cycle counters are summed over the chip (`SQ_BUSY_CU_CYCLES` over 256 CUs, "
+              "`SQ_VALU_MFMA_BUSY_CYCLES` over 1024 SIMDs; the latter equals 32 x the MFMA "
+              "count, one 32x32x16 MFMA taking 32 clocks).  Effective clock = "
+              "`SQ_BUSY_CU_CYCLES` / 256 / kernel duration.", "",
+              "| kernel | duration (ms, under counters) | effective clock (GHz) | MFMA busy | LDS busy "
+              "| LDS bank-conflict share | VALU / MFMA | LDS / MFMA | SALU / MFMA | wait-any / wave cycles |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
+    for key, c in agg.items():
+        m = {k: sum(v) / len(v) for k, v in c.items()}
+        t = sum(dur[key].values()) / len(dur[key])
+        busy = m["SQ_BUSY_CU_CYCLES"]
+        lines.append(
+            f"| `{KERNELS[key][0]}` | {t * 1e3:.2f} | {busy / n_cu / t / 1e9:.2f} | "
+            f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * busy):.3f} | "
+            f"{m['SQ_LDS_IDX_ACTIVE'] / busy:.3f} | "
+            f"{m['SQ_LDS_BANK_CONFLICT'] / max(m['SQ_LDS_IDX_ACTIVE'], 1):.3f} | "
+            f"{m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f} | "
+            f"{m['SQ_INSTS_LDS'] / m['SQ_INSTS_MFMA']:.2f} | "
+            f"{m['SQ_INSTS_SALU'] / m['SQ_INSTS_MFMA']:.2f} | "
+            f"{m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.3f} |")
+    lines.append("")
     return "\n".join(lines)
 
 
@@ -226,6 +282,9 @@ def main():
     args = parse()
     if args.pmc_summary:
         print(pmc_summary(args.pmc_summary, args.workload))
+        return
+    if args.sq_summary:
+        print(sq_summary(args.sq_summary, args.workload))
         return
     if args.copy_probe:
         copy_probe(args.copy_probe)
