@@ -235,12 +235,13 @@ def cpu_baseline(w, arrays, target_s):
         t_idx = np.sort(rng.choice(rows_all.size, size=min(n, rows_all.size), replace=False))
         rows = rows_all[t_idx]
         t0 = time.perf_counter()
+        dQ = None
         if w.backward:
             dO = arrays["do"][:, :1][:, :, rows]
-            oracle.attention_bwd(arrays["q"], arrays["k"], arrays["v"], dO, rows, w.causal,
-                                 heads=[0], bounds=bounds)
-        oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal, heads=[0],
-                             bounds=bounds)
+            dQ, _, _ = oracle.attention_bwd(arrays["q"], arrays["k"], arrays["v"], dO, rows,
+                                            w.causal, heads=[0], bounds=bounds)
+        O, LSE = oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal,
+                                      heads=[0], bounds=bounds)
         dt = time.perf_counter() - t0
         if dt >= 0.6 * target_s or n >= rows_all.size:
             break
@@ -265,7 +266,40 @@ def cpu_baseline(w, arrays, target_s):
             "sample": f"{rows.size} query rows of head 0 (batch {w.batch}), "
                       f"{'forward + backward' if w.backward else 'forward'} in fp64, "
                       f"{pairs:.3e} visible pairs, {dt:.1f} s wall, BLAS {blas}",
-            "seconds": dt}
+            "seconds": dt}, (t_idx, O, LSE, dQ)
+
+
+def sample_parity(w, ref, out, lse, dq):
+    """The timed run's outputs on the oracle's sample rows (head 0) against the oracle."""
+    import numpy as np
+    t_idx, O, LSE, dQ = ref
+    d = w.head_dim
+    ti = torch_index(t_idx, out.device)
+
+    def cmp(got, want):
+        err = np.abs(got - want)
+        den = np.linalg.norm(want)
+        return {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
+                "rel_fro": float(np.linalg.norm(got - want) / den) if den > 0 else 0.0}
+
+    res = {"rows": int(t_idx.size), "head": 0}
+    res["o"] = cmp(out[:, :1][:, :, ti].float().cpu().numpy()[..., :d], O)
+    lg = lse[:, :1][:, :, ti].cpu().numpy()
+    fin = np.isfinite(LSE)
+    res["lse_max_abs"] = float(np.abs(lg[fin] - LSE[fin]).max()) if fin.any() else 0.0
+    res["lse_inf_rows_match"] = bool(np.array_equal(np.isneginf(lg), np.isneginf(LSE)))
+    if dQ is not None and dq is not None:
+        res["dq"] = cmp(dq[:, :1][:, :, ti].cpu().numpy()[..., :d], dQ)
+    tol = (2e-2, 2e-3, 1e-2) if w.dtype == "bf16" else (1e-5, 1e-5, 1e-5)
+    ok = all(res[k]["max_abs"] <= tol[0] and res[k]["mean_abs"] <= tol[1]
+             and res[k]["rel_fro"] <= tol[2] for k in ("o", "dq") if k in res)
+    res["pass"] = bool(ok and res["lse_max_abs"] <= 1e-3 and res["lse_inf_rows_match"])
+    return res
+
+
+def torch_index(idx, device):
+    import torch
+    return torch.from_numpy(idx).to(device)
 
 
 def copy_probe(nbytes):
@@ -439,9 +473,12 @@ def main():
                        "traffic": measured_traffic(w.name, name),
                        "kernel": name, "avg_launch_ms": round(launch_ms, 4),
                        "flop_per_launch": per_launch_flop}
+    if res["roofline"]["traffic"] is not None:
+        res["roofline"]["traffic_gbps"] = round(res["roofline"]["traffic"] / (launch_ms * 1e-3) / 1e9, 1)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, arrays, args.cpu_seconds)
+        res["cpu_baseline"], ref = cpu_baseline(w, arrays, args.cpu_seconds)
+        res["parity"] = sample_parity(w, ref, out, lse, dq if w.backward else None)
     print(json.dumps(res), flush=True)
 
 
