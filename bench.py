@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run one device-to-device copy of BYTES (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
+    ap.add_argument("--aux", action="store_true",
+                    help="time the HBM-bound helper kernels (standalone LSE merge, delta) "
+                         "instead of the step and print one JSON line")
     ap.add_argument("--sq-summary", metavar="DIR", default=None,
                     help="print the markdown summary of the three SQ-counter --pmc runs under "
                          "DIR (cnt_1/, cnt_2/, cnt_3/) and exit")
@@ -312,8 +315,71 @@ def copy_probe(nbytes):
     print(json.dumps({"copy_probe_bytes": nbytes}), flush=True)
 
 
+def aux_bench(reps=50):
+    """The HBM-bound helpers against the 8 TB/s roofline, at the llama_share and
+    zigzag_fwdbwd shapes: the standalone LSE merge (rows x d fp32 partials) and the
+    backward's delta = rowsum(dO * O) (bf16 inputs).  Algorithmic bytes per row:
+    the merge reads both partials (2 d x 4 B) and both LSEs and writes the accumulator
+    (d x 4 B) and its LSE, (3 d + 3) x 4 B in all; delta reads O and dO (2 d x 2 B)
+    and writes 4 B."""
+    import torch
+
+    from ring_context_parallelism_amd import ra
+    dev = torch.device("cuda:0")
+    ra.lib()
+    out = {"metric": "HBM-bound helper kernels, achieved GB/s", "unit": "GB/s", "kernels": []}
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for name, rows, d in (("llama_share", 1 * 16 * 8192, 128), ("zigzag_fwdbwd", 16 * 65536, 128)):
+        oa = torch.randn(rows, d, device=dev)
+        op = torch.randn(rows, d, device=dev)
+        la = torch.randn(rows, device=dev)
+        lp = torch.randn(rows, device=dev)
+        ms = timed(lambda: ra.ra_lse_merge(rows, d, oa, la, op, lp, stream=stream))
+        nbytes = rows * (3 * d * 4 + 3 * 4)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out["kernels"].append({"kernel": "lse_merge_kernel", "shape": f"{name}: {rows} rows x {d}",
+                               "ms": round(ms, 4), "bytes": nbytes, "achieved": round(gbs, 1),
+                               "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    # reference: a plain device-to-device copy of 1 GiB (read + write)
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src))
+    gbs = 2 * src.numel() * 4 / (ms * 1e-3) / 1e9
+    out["copy_reference"] = {"bytes": 2 * src.numel() * 4, "ms": round(ms, 4),
+                             "achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del src, dst
+    B, H, L, D = 1, 16, 65536, 128
+    o = torch.randn(B, H, L, D, device=dev).to(torch.bfloat16)
+    do = torch.randn(B, H, L, D, device=dev).to(torch.bfloat16)
+    delta = torch.empty(B, H, L, device=dev)
+    prob = ra.make_problem(batch=B, heads_q=H, heads_kv=H, head_dim=D, head_dim_padded=D,
+                           seq_total=2 * L, world=2, layout="zigzag", causal=True, dtype="bf16")
+    ms = timed(lambda: ra.ra_bwd_delta(prob, o, do, delta, stream=stream))
+    nbytes = B * H * L * (2 * D * 2 + 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out["kernels"].append({"kernel": "bwd_delta_kernel", "shape": f"zigzag_fwdbwd: {B * H * L} rows x {D}",
+                           "ms": round(ms, 4), "bytes": nbytes, "achieved": round(gbs, 1),
+                           "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
+    if args.aux:
+        aux_bench()
+        return
     if args.pmc_summary:
         print(pmc_summary(args.pmc_summary, args.workload))
         return

@@ -50,37 +50,47 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(int64_t rows, int32_t d4
 
 // delta[row] = sum_d dout[row, d] * out[row, d]; one row per group of G lanes, each
 // lane reading 16 bytes of both tensors, then a butterfly reduction inside the group.
+// Rows of one (batch, head) per workgroup block: G lanes share a row (16 bytes of
+// each operand per lane), 256 / G rows per pass, kDeltaPasses passes whose loads are
+// all issued before any is used.  Workgroup -> (b*H + h, row block) is one scalar
+// division per workgroup.
+constexpr int kDeltaPasses = 4;
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(int32_t B, int32_t H, int32_t L,
+__global__ __launch_bounds__(256) void bwd_delta_kernel(int32_t H, int32_t L, int32_t n_blk,
                                                         const T* out, const T* dout, int64_t sb,
                                                         int64_t sh, int64_t st, float* delta) {
   constexpr int EPL = 16 / sizeof(T);  // elements per lane
   constexpr int G = D / EPL;           // lanes per row
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = gid / G;
-  const int c = (int)(gid % G);
-  const int64_t nrows = (int64_t)B * H * L;
-  float acc = 0.0f;
-  if (row < nrows) {
-    const int64_t t = row % L, bh = row / L;
-    const int64_t h = bh % H, b = bh / H;
-    const int64_t off = b * sb + h * sh + t * st + (int64_t)c * EPL;
-    if constexpr (sizeof(T) == 2) {
-      typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-      const bf16x8 x = *(const bf16x8*)(out + off);
-      const bf16x8 y = *(const bf16x8*)(dout + off);
+  constexpr int RPP = 256 / G;         // rows per pass
+  typedef T vec_t __attribute__((ext_vector_type(EPL)));
+  const int bh = blockIdx.x / n_blk, blk = blockIdx.x % n_blk;
+  const int h = bh % H, b = bh / H;
+  const int c = threadIdx.x % G, r = threadIdx.x / G;
+  const T* ob = out + (int64_t)b * sb + (int64_t)h * sh + c * EPL;
+  const T* db = dout + (int64_t)b * sb + (int64_t)h * sh + c * EPL;
+  vec_t x[kDeltaPasses], y[kDeltaPasses];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc += (float)x[e] * (float)y[e];
+  for (int p = 0; p < kDeltaPasses; ++p) {
+    const int t = (blk * kDeltaPasses + p) * RPP + r;
+    if (t < L) {
+      x[p] = *(const vec_t*)(ob + (int64_t)t * st);
+      y[p] = *(const vec_t*)(db + (int64_t)t * st);
     } else {
-      const f32x4 x = *(const f32x4*)(out + off);
-      const f32x4 y = *(const f32x4*)(dout + off);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc += x[e] * y[e];
+      x[p] = vec_t{};
+      y[p] = vec_t{};
     }
   }
 #pragma unroll
-  for (int m = G / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < nrows && c == 0) delta[row] = acc;
+  for (int p = 0; p < kDeltaPasses; ++p) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc += (float)x[p][e] * (float)y[p][e];
+#pragma unroll
+    for (int m = G / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+    const int t = (blk * kDeltaPasses + p) * RPP + r;
+    if (t < L && c == 0) delta[(int64_t)bh * L + t] = acc;
+  }
 }
 
 __global__ __launch_bounds__(256) void fill_kernel(float* p, int64_t n, float value) {
@@ -96,11 +106,11 @@ __global__ __launch_bounds__(256) void fill_kernel(float* p, int64_t n, float va
 template <typename T, int D>
 hipError_t delta_launch(int32_t B, int32_t H, int32_t L, const void* out, const void* dout,
                         int64_t sb, int64_t sh, int64_t st, float* delta, hipStream_t s) {
-  constexpr int G = D / (16 / (int)sizeof(T));
-  const int64_t threads = (int64_t)B * H * L * G;
-  const int64_t blocks = (threads + 255) / 256;
-  hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, B, H, L,
-                     (const T*)out, (const T*)dout, sb, sh, st, delta);
+  constexpr int RPB = 256 / (D / (16 / (int)sizeof(T))) * kDeltaPasses;  // rows per block
+  const int32_t n_blk = (L + RPB - 1) / RPB;
+  const int64_t blocks = (int64_t)B * H * n_blk;
+  hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, H, L,
+                     n_blk, (const T*)out, (const T*)dout, sb, sh, st, delta);
   return hipGetLastError();
 }
 
