@@ -18,11 +18,12 @@
 //    waves sharing a SIMD belong to different workgroups and their barriers do not
 //    keep them in step.
 //
-//  * dQ kernel -- the forward's shape: one workgroup = 4 waves = 128 query rows of
+//  * dQ kernel -- the forward's shape: one workgroup = 8 waves = 256 query rows of
 //    one (batch, query head), KV tiles of 32 keys streamed through double-buffered
-//    LDS.  Scores are computed transposed, S^T = K Q^T, so every lane holds one
-//    query row; P^T and dS^T = P^T o (dP^T - delta) feed dQ^T += K^T dS^T from
-//    registers, with K^T read by LDS transpose loads.  Two workgroups per CU.
+//    LDS (each tile serves all 256 rows).  Scores are computed transposed,
+//    S^T = K Q^T, so every lane holds one query row; P^T and
+//    dS^T = P^T o (dP^T - delta) feed dQ^T += K^T dS^T from registers, with K^T
+//    read by LDS transpose loads.
 //
 // The dQ kernel recomputes S and dP (7 MFMA passes in all instead of 5); in
 // exchange no dS exchange, no cross-workgroup reduction and no atomics remain.
@@ -371,12 +372,12 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------- dQ kernel
 
-constexpr int kQThreads = 256;  // 4 waves
-constexpr int kQBM = 128;       // query rows per workgroup
+constexpr int kQThreads = 512;  // 8 waves
+constexpr int kQBM = 256;       // query rows per workgroup
 constexpr int kQBN = 32;        // keys per KV tile
 
 template <int D, bool PACKED>
-__global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   constexpr int NKB = D / 16;
   constexpr int ND = D / 32;
   constexpr int NB = kQBN / 32;
