@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--sq-summary", metavar="DIR", default=None,
                     help="print the markdown summary of the three SQ-counter --pmc runs under "
                          "DIR (cnt_1/, cnt_2/, cnt_3/) and exit")
+    ap.add_argument("--trace-summary", metavar="DIR", default=None,
+                    help="print the markdown summary of the rocprofv3 --kernel-trace --stats run "
+                         "under DIR (run_kernel_stats.csv, and the bench line in DIR.log) and exit")
     ap.add_argument("--pmc-summary", metavar="DIR", default=None,
                     help="print the markdown traffic summary of the rocprofv3 --pmc runs under "
                          "DIR (pmc_fetch/, pmc_write/, pmc_copy_fetch/, pmc_copy_write/) and exit")
@@ -179,6 +182,68 @@ def sq_summary(root, workload, n_cu=256):
             f"{m['SQ_INSTS_LDS'] / m['SQ_INSTS_MFMA']:.2f} | "
             f"{m['SQ_INSTS_SALU'] / m['SQ_INSTS_MFMA']:.2f} | "
             f"{m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.3f} |")
+    lines.append("")
+    return "\n".join(lines)
+
+
+def trace_summary(run_dir, workload):
+    """Kernel durations from a --kernel-trace --stats run, with the algorithmic FLOP rate of
+    each attention kernel (forward 4d, dK/dV 8d, dQ 2d per visible pair and head)."""
+    from ring_context_parallelism_amd import ra
+    from ring_context_parallelism_amd.workloads import WORKLOADS, document_bounds
+    w = WORKLOADS[workload]
+    bounds = document_bounds(w) if w.docs else None
+    prob = ra.make_problem(batch=w.batch, heads_q=w.heads_q, heads_kv=w.heads_kv,
+                           head_dim=w.head_dim, head_dim_padded=w.head_dim_padded,
+                           seq_total=w.seq_total, world=w.world, layout=w.layout,
+                           causal=w.causal, dtype=w.dtype)
+    steps = step_flops(w, prob, ra, bounds)
+    pairs = sum(st["visible_pairs_per_head"] * w.batch * w.heads_q for st in steps) / len(steps)
+    per_pair = {"fwd_bf16_kernel": 4, "fwd_f32_kernel": 4, "bwd_dkdv_kernel": 8,
+                "bwd_dq_kernel": 2}
+    peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
+    rows = list(csv.DictReader(open(os.path.join(run_dir, "run_kernel_stats.csv"))))
+    bench_line = None
+    log = run_dir.rstrip("/") + ".log"
+    if os.path.exists(log):
+        for line in open(log):
+            if line.startswith("{") and '"roofline"' in line:
+                bench_line = json.loads(line)
+    lines = [f"# Kernel durations: {workload} workload ({w.batch} x {w.heads_q} heads x "
+             f"d{w.head_dim}, S={w.seq_total}, {w.layout} p={w.world}, rank {w.rank}, {w.dtype})",
+             "", "Command (run from /tmp on one MI355X):", "", "```",
+             "cd /tmp && timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv "
+             "-d <out>/prof_default -o run -- python3 <repo>/bench.py --workload "
+             f"{workload} --steps 3 --warmup 1 --no-cpu-baseline > <out>/prof_default.log",
+             f"python3 <repo>/bench.py --workload {workload} --trace-summary <out>/prof_default",
+             "```", "",
+             f"{len(steps)} live ring steps per bench step; {pairs:.4g} visible (query, key) pairs "
+             "per launch summed over batch and heads.  Algorithmic FLOP per launch: forward 4d, "
+             "dK/dV kernel 8d (S, dP, dV, dK), dQ kernel 2d (its recomputation of S and dP is "
+             "not counted) per pair.", "",
+             "| kernel | calls | average (ms) | min (ms) | max (ms) | share | algorithmic "
+             "TFLOP/s | of peak |", "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        avg = float(r["AverageNs"]) * 1e-6
+        rate = ""
+        frac = ""
+        for sub, k in per_pair.items():
+            if sub in r["Name"]:
+                tf = k * w.head_dim * pairs / (avg * 1e-3) / 1e12
+                rate, frac = f"{tf:.1f}", f"{100 * tf / peak:.1f}%"
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {avg:.3f} | "
+                     f"{float(r['MinNs']) * 1e-6:.3f} | {float(r['MaxNs']) * 1e-6:.3f} | "
+                     f"{float(r['Percentage']):.2f}% | {rate} | {frac} |")
+    if bench_line is not None:
+        rf = bench_line["roofline"]
+        lines += ["", "The bench line printed by the same profiled command (HIP events on the "
+                  "launch stream, timed steps only; the rocprof averages include the warmup "
+                  f"step): {bench_line['value']:.1f} TFLOP/s per step, forward "
+                  f"{bench_line['fwd']['pct_peak']:.1f}% of peak"
+                  + (f", backward {bench_line['bwd']['pct_peak']:.1f}%" if "bwd" in bench_line
+                     else "")
+                  + f"; roofline kernel `{rf['kernel']}` {rf['avg_launch_ms']:.3f} ms per launch, "
+                  f"{rf['achieved']:.1f} TFLOP/s, frac {rf['frac']:.4f}."]
     lines.append("")
     return "\n".join(lines)
 
@@ -382,6 +447,9 @@ def main():
         return
     if args.pmc_summary:
         print(pmc_summary(args.pmc_summary, args.workload))
+        return
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.workload))
         return
     if args.sq_summary:
         print(sq_summary(args.sq_summary, args.workload))
