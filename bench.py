@@ -165,10 +165,13 @@ def sq_summary(root, workload, n_cu=256):
               "Cycle counters are summed over the chip (`SQ_BUSY_CU_CYCLES` over 256 CUs, "
               "`SQ_VALU_MFMA_BUSY_CYCLES` over 1024 SIMDs; the latter equals 32 x the MFMA "
               "count, one 32x32x16 MFMA taking 32 clocks).  Effective clock = "
-              "`SQ_BUSY_CU_CYCLES` / 256 / kernel duration.", "",
+              "`SQ_BUSY_CU_CYCLES` / 256 / kernel duration.  VALU instructions per SIMD-cycle = "
+              "`SQ_INSTS_VALU` / (4 `SQ_BUSY_CU_CYCLES`); waves per SIMD = `SQ_WAVE_CYCLES` / "
+              "`SQ_BUSY_CU_CYCLES` (`SQ_WAVE_CYCLES` counts in units of 4 cycles).", "",
               "| kernel | duration (ms, under counters) | effective clock (GHz) | MFMA busy | LDS busy "
-              "| LDS bank-conflict share | VALU / MFMA | LDS / MFMA | SALU / MFMA | wait-any / wave cycles |",
-              "|---|---|---|---|---|---|---|---|---|---|"]
+              "| LDS bank-conflict share | VALU / MFMA | LDS / MFMA | SALU / MFMA | wait-any / wave cycles "
+              "| VALU instr per SIMD-cycle | waves per SIMD |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for key, c in agg.items():
         m = {k: sum(v) / len(v) for k, v in c.items()}
         t = sum(dur[key].values()) / len(dur[key])
@@ -181,7 +184,8 @@ def sq_summary(root, workload, n_cu=256):
             f"{m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f} | "
             f"{m['SQ_INSTS_LDS'] / m['SQ_INSTS_MFMA']:.2f} | "
             f"{m['SQ_INSTS_SALU'] / m['SQ_INSTS_MFMA']:.2f} | "
-            f"{m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.3f} |")
+            f"{m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.3f} | "
+            f"{m['SQ_INSTS_VALU'] / (4 * busy):.3f} | {m['SQ_WAVE_CYCLES'] / busy:.2f} |")
     lines.append("")
     return "\n".join(lines)
 

@@ -23,7 +23,8 @@ Workloads (sizes from the pages' own models):
   tabular_rows  -- nanoTabPFN-shaped (1, 150000 rows, 5 features, embed 96), 4 heads
                    x d 24 stored padded to 32, attention over rows with the feature
                    axis folded into the batch, p 4, rank 0, non-causal, U(-1,1), fp32
-                   and bf16 (Mosaic post, "The Problem" / "The Implementation")
+                   and bf16 (Mosaic post, "The Problem" / "The Implementation");
+                   tabular_rows_bf16 is the same draw in bf16
   zigzag_fwdbwd -- 16 heads x d 128, S 131072, p 2 zigzag, rank 0, causal, forward
                    then backward, N(0,1)*0.5 including dO, bf16
   packed_fwdbwd -- zigzag_fwdbwd's shape with packed documents and right padding
@@ -88,6 +89,9 @@ WORKLOADS = {
                             "striped", 3, True, "normal", 1.0),
     "tabular_rows": Workload("tabular_rows", 3, "f32", 5, 4, 4, 24, 32, 150000, 4,
                              "contiguous", 0, False, "uniform", 1.0, fold=(150000, 5, 96)),
+    "tabular_rows_bf16": Workload("tabular_rows_bf16", 3, "bf16", 5, 4, 4, 24, 32, 150000, 4,
+                                  "contiguous", 0, False, "uniform", 1.0,
+                                  fold=(150000, 5, 96)),
     "zigzag_fwdbwd": Workload("zigzag_fwdbwd", 4, "bf16", 1, 16, 16, 128, 128, 131072, 2,
                               "zigzag", 0, True, "normal", 0.5, backward=True),
     "packed_fwdbwd": Workload("packed_fwdbwd", 5, "bf16", 1, 16, 16, 128, 128, 131072, 2,
