@@ -11,12 +11,13 @@
 //
 //  * dK/dV kernel -- one workgroup = 4 waves = 128 keys of one (batch, KV head);
 //    each wave owns 32 keys and walks every 32-row query tile that sees them.
-//    Scores are computed as S[q][key] (every lane holds one key and 16 query rows),
-//    so P and dS feed dV^T = dO^T P and dK^T = Q^T dS straight from registers.
-//    Each lane's K row stays in registers and V in LDS; query tiles (Q, dO, LSE,
-//    delta) stream through double-buffered LDS.  Two workgroups per CU, so the two
-//    waves sharing a SIMD belong to different workgroups and their barriers do not
-//    keep them in step.
+//    Scores are computed as S[q][key] on 16x16x32 MFMA tiles (every lane holds two
+//    keys and 8 query rows), so P and dS feed dV^T = dO^T P and dK^T = Q^T dS
+//    straight from registers.  Each lane's K rows stay in registers and V in LDS;
+//    query tiles (Q, dO) stream through double-buffered LDS, and LSE and delta reach
+//    LDS through registers, pre-scaled.  Two workgroups per CU, so the two waves
+//    sharing a SIMD belong to different workgroups and their barriers do not keep
+//    them in step.
 //
 //  * dQ kernel -- the forward's shape: one workgroup = 8 waves = 256 query rows of
 //    one (batch, query head), KV tiles of 32 keys streamed through double-buffered
@@ -147,11 +148,31 @@ constexpr int kKvThreads = 256;  // 4 waves, each 32 keys
 constexpr int kKvBN = 128;       // keys per workgroup
 constexpr int kKvBQ = 32;        // query rows per iteration
 
+// Tile row order of the 16x16x32 operands: logical row m = 16 h + 4 g + k (h: query
+// half, g: transpose-read lane group, k: row within the group) lives in tile row
+// 16 h + 2 (4 (g & 1) + k) + (g >> 1).  16-byte reads of the 16 rows of a half
+// touch 16 distinct rows, and a transpose read (lane groups {0,1} or {2,3}, 8 rows x
+// 2 chunks) touches 8 rows of one parity; with the odd padded stride both are
+// conflict free.
+__device__ inline int rho16(int m) {
+  const int g = (m >> 2) & 3;
+  return (m & 16) | ((((g & 1) << 2) | (m & 3)) << 1) | (g >> 1);
+}
+
 // PACKED: packed documents (a.seg != nullptr), a separate instantiation.
+//
+// 16x16x32 MFMA tiles (a stream of them sustains about 15% more FLOP/s than
+// 32x32x16 tiles under the board power limit, and this kernel runs at that limit).
+// Accumulator layout of a 16x16 tile: lane l holds column l % 16 and rows
+// 4 (l / 16) + r; operands hold row (A) or column (B) l % 16 and contraction
+// indices 8 (l / 16) + j.  S and dP are computed as [query][key] tiles, so each lane
+// holds two keys (l % 16 and 16 + l % 16 of the wave's 32) and 8 query rows, and P
+// and dS feed dV^T += dO^T P and dK^T += Q^T dS from registers: contraction slot
+// 8 g + j holds logical query row 4 g + j (j < 4) or 16 + 4 g + j - 4.
 template <int D, bool PACKED>
 __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int NKB = D / 16;  // 16-wide head-dim blocks (S and dP contractions)
-  constexpr int NDB = D / 32;  // 32-row head-dim blocks of dK^T, dV^T
+  constexpr int NKK = D / 32;  // 32-wide head-dim steps of the S and dP contractions
+  constexpr int NDT = D / 16;  // 16-row head-dim tiles of dK^T, dV^T
   using PQ = Pad<D>;
   constexpr int PS = PQ::PS;
   constexpr int QEL = PQ::slots(kKvBQ) * 8;
@@ -171,7 +192,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int l32 = lane & 31, hh = lane >> 5;
+  const int l16 = lane & 15, grp = lane >> 4;
   const int kw = wave;  // 32-key block of this wave
   const int L = a.map.L;
 
@@ -180,36 +201,63 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int bg = logical / a.n_ktiles;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int u0 = kt * kKvBN;
-  const int krow = kw * 32 + l32;  // this lane's key within the tile
-  const int key = u0 + krow;
-  const bool key_ok = key < L;
+  int krow[2], key[2];
+  bool key_ok[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    krow[x] = kw * 32 + x * 16 + l16;  // this lane's keys within the tile
+    key[x] = u0 + krow[x];
+    key_ok[x] = key[x] < L;
+  }
 
   const __bf16* kb = (const __bf16*)a.k + (int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh;
   const __bf16* vb = (const __bf16*)a.v + (int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh;
   const uint32_t kv_row = (uint32_t)(a.kv_st * 2);
 
-  // Queries [q_lo, q_hi) of chunk cq that see this lane's key; query tiles from
-  // t_first to t_end hold those of every key, and rows in [full_lo, full_hi) see
-  // every key of the workgroup (no mask).
-  int q_lo = 0, q_hi = L, t_first = 0, t_end = L, full_lo = 0, full_hi = L;
+  // Queries [q_lo, q_hi) of chunk cq that see each of this lane's keys; query tiles
+  // from t_first to t_end hold those of every key, and rows in [full_lo, full_hi)
+  // see every key of the workgroup (no mask).
+  int q_lo[2] = {0, 0}, q_hi[2] = {L, L};
+  int t_first = 0, t_end = L, full_lo = 0, full_hi = L;
   if constexpr (PACKED) {  // packed documents
     __shared__ int red[4];
-    if (key_ok) {
-      query_interval(a.map, a.cq, pos_of(a.map, a.ck, key), a.causal,
-                     a.seg + (int64_t)b * a.seg_n, a.seg_n, q_lo, q_hi);
-    } else {
-      q_lo = L;
-      q_hi = 0;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      if (key_ok[x]) {
+        query_interval(a.map, a.cq, pos_of(a.map, a.ck, key[x]), a.causal,
+                       a.seg + (int64_t)b * a.seg_n, a.seg_n, q_lo[x], q_hi[x]);
+      } else {
+        q_lo[x] = L;
+        q_hi[x] = 0;
+      }
     }
-    wg_interval_reduce(red, q_lo, q_hi, L, t_first, t_end, full_lo, full_hi);
+    if (tid == 0) {
+      red[0] = L;
+      red[1] = 0;
+      red[2] = 0;
+      red[3] = L;
+    }
+    __syncthreads();
+    atomicMin(&red[0], min(q_lo[0], q_lo[1]));
+    atomicMax(&red[1], max(q_hi[0], q_hi[1]));
+    atomicMax(&red[2], max(q_lo[0], q_lo[1]));
+    atomicMin(&red[3], min(q_hi[0], q_hi[1]));
+    __syncthreads();
+    t_first = red[0];
+    t_end = red[1];
+    full_lo = red[2];
+    full_hi = red[3];
   } else {  // dense: query t sees key u iff t >= count_le(cq, pos(ck, u) - 1)
     const int u_last = min(u0 + kKvBN, L) - 1;
     if (a.causal) {
       t_first = count_le(a.map, a.cq, pos_of(a.map, a.ck, u0) - 1);
       full_lo = count_le(a.map, a.cq, pos_of(a.map, a.ck, u_last) - 1);
-      q_lo = key_ok ? count_le(a.map, a.cq, pos_of(a.map, a.ck, key) - 1) : L;
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        q_lo[x] = key_ok[x] ? count_le(a.map, a.cq, pos_of(a.map, a.ck, key[x]) - 1) : L;
     } else {
-      q_lo = key_ok ? 0 : L;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) q_lo[x] = key_ok[x] ? 0 : L;
     }
     if (u0 + kKvBN > L) full_lo = L;  // ragged key tile: always mask
   }
@@ -219,11 +267,11 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int n_iter = per_head > 0 ? per_head * a.group : 0;
   if (n_iter == 0) return;  // no query of this chunk sees these keys
 
-  f32x16 dv_t[NDB], dk_t[NDB];
+  f32x4 dv_t[NDT][2], dk_t[NDT][2];  // [head-dim tile][key tile]
 #pragma unroll
-  for (int n = 0; n < NDB; ++n) {
-    dv_t[n] = f32x16{};
-    dk_t[n] = f32x16{};
+  for (int n = 0; n < NDT; ++n) {
+    dv_t[n][0] = dv_t[n][1] = f32x4{};
+    dk_t[n][0] = dk_t[n][1] = f32x4{};
   }
 
   // Iterations walk the query tiles [t_lo, t_hi) of one head, then the next head of
@@ -234,45 +282,66 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int h0 = g * a.group;
   const __bf16* nq = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h0 * a.q_sh;
   const __bf16* no = (const __bf16*)a.dout + (int64_t)b * a.o_sb + (int64_t)h0 * a.o_sh;
-  const float* nst = (wave == 0 ? a.lse : a.delta) + ((int64_t)b * a.Hq + h0) * L;
   int nt = t_lo;   // first row of the next DMA's tile
   int ct = t_lo;   // first row of the current step's tile
-  auto dma_q = [&](__bf16* qn, __bf16* don, float* lsn, float* dln) {
+  auto dma_q = [&](__bf16* qn, __bf16* don) {
     dma_pad<kKvBQ, D, kKvThreads>(make_rsrc(nq, (uint32_t)L * q_row), q_row, nt, qn, wave, lane);
     dma_pad<kKvBQ, D, kKvThreads>(make_rsrc(no, (uint32_t)L * o_row), o_row, nt, don, wave, lane);
-    if (wave < 2) {  // rows past the chunk end read as 0: Q = dO = delta = 0 gives dS = 0
-      // slot s holds the statistic of query row (s & 32) + rho(s & 31) of the tile
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(nst, (uint32_t)L * 4u),
-                                               (lds_void_t*)(wave == 0 ? lsn : dln), 4,
-                                               (uint32_t)(nt + (lane & 32) + rho(lane & 31)) * 4u,
-                                               0, 0, 0);
-    }
     nt += kKvBQ;
     if (nt >= t_hi) {
       nt = t_lo;
       nq += a.q_sh;
       no += a.o_sh;
-      nst += L;
+    }
+  };
+  // Row statistics pass through registers one tile ahead of their LDS slots, so they
+  // are stored transformed: wave 0 keeps LSE * log2 e (the exponent is one FMA),
+  // wave 1 keeps -delta (the dP accumulator starts from it).  Slot s holds logical
+  // row s: tile row (s & 32) + rho16(s & 31); rows past the chunk end read as 0,
+  // where Q = dO = 0 gives dS = dV = 0.  The LDS write of tile j's statistic comes
+  // before the step's DMA issue and the load of tile j + 1's after it.
+  const float* sst = (wave == 0 ? a.lse : a.delta) + ((int64_t)b * a.Hq + h0) * L;
+  int st_row = t_lo;
+  const uint32_t st_lane = (uint32_t)((lane & 32) + rho16(lane & 31));
+  float stat_next = 0.0f;
+  auto stat_write = [&](float* lsn, float* dln) {
+    if (wave == 0) lsn[lane] = stat_next * kLog2e;
+    if (wave == 1) dln[lane] = -stat_next;
+  };
+  auto stat_prefetch = [&](int it_next) {
+    if (wave < 2 && it_next < n_iter) {
+      stat_next = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(sst, (uint32_t)L * 4u),
+                                                      ((uint32_t)st_row + st_lane) * 4u, 0, 0));
+      st_row += kKvBQ;
+      if (st_row >= t_hi) {
+        st_row = t_lo;
+        sst += L;
+      }
     }
   };
 
-  // This lane's key row of K as the B operand of S = Q K^T, held in registers for
-  // the whole kernel (rows past the chunk end read as 0): the K tile is never
-  // re-read from LDS.
-  bf16x8 kreg[NKB];
+  // This lane's two key rows of K as B operands of S = Q K^T, held in registers for
+  // the whole kernel (rows past the chunk end read as 0).
+  bf16x8 kreg[2][NKK];
   {
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, (uint32_t)L * kv_row);
 #pragma unroll
-    for (int kk = 0; kk < NKB; ++kk)
-      kreg[kk] = load_row8(kr, (uint32_t)key * kv_row + (uint32_t)(kk * 32 + hh * 16));
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        kreg[x][kk] = load_row8(kr, (uint32_t)key[x] * kv_row + (uint32_t)(kk * 64 + grp * 16));
   }
-  // Transpose-read source slot of this lane: lane j of each 16-lane group receives
-  // rows r..r+3 at column c + j of the slot it and its group point at.
-  const int src_row = (lane & 15) >> 2;
-  const int src_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-  // This lane's query row as an A-operand row: accumulator row m of S and dP is
-  // query row rho(m) of the tile.
-  const int qrow = rho(l32);
+  // A-operand rows of S and dP: logical rows 16 h + l16; transpose-read sources:
+  // logical rows 16 h + 4 grp + l16 / 4, columns 4 (l16 % 4) of a 16-column tile.
+  int arow[2], trow[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    arow[hf] = rho16(hf * 16 + l16) * PS + grp * 8;
+    trow[hf] = rho16(hf * 16 + grp * 4 + (l16 >> 2)) * PS + (l16 & 3) * 4;
+  }
+  // Tile row of accumulator row r of query half hf: 16 hf + 2 r + goff.
+  const int goff = 8 * (grp & 1) + (grp >> 1);
 
   auto step = [&](int it, const __bf16* qt, const __bf16* dot, const float* ls,
                   const float* dl, __bf16* qn, __bf16* don, float* lsn, float* dln) {
@@ -280,93 +349,128 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     ct = ct + kKvBQ >= t_hi ? t_lo : ct + kKvBQ;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile `it`
     __syncthreads();                     // every wave's; tile it-1 is free
-    if (it + 1 < n_iter) dma_q(qn, don, lsn, dln);
+    if (it + 1 < n_iter) {
+      stat_write(lsn, dln);
+      dma_q(qn, don);
+      stat_prefetch(it + 2);
+    }
     __builtin_amdgcn_iglp_opt(0);  // scheduling hint: interleave LDS reads with MFMAs
 
-    // S[q][key], dP[q][key] for the tile's 32 query rows and this wave's 32 keys.
-    f32x16 s = {}, dp = {};
+    // S[q][key] and dP[q][key] - delta[q] for the tile's two 16-row halves and this
+    // lane's keys.
+    f32x4 s[2][2], dp[2][2];  // [query half][key tile]
 #pragma unroll
-    for (int kk = 0; kk < NKB; ++kk) {
-      const int col = kk * 16 + hh * 8;
-      const bf16x8 qa = *(const bf16x8*)(qt + qrow * PS + col);
-      const bf16x8 da = *(const bf16x8*)(dot + qrow * PS + col);
-      const bf16x8 kbv = kreg[kk];
-      const bf16x8 vbv = *(const bf16x8*)(s_v + xoff<D>(krow, col));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kbv, s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vbv, dp, 0, 0, 0);
+    for (int hf = 0; hf < 2; ++hf) {
+      const f32x4 nd = *(const f32x4*)(dl + hf * 16 + grp * 4);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        s[hf][x] = f32x4{};
+        dp[hf][x] = nd;
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      bf16x8 vbv[2], qa[2], da[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        vbv[x] = *(const bf16x8*)(s_v + xoff<D>(krow[x], kk * 32 + grp * 8));
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        qa[hf] = *(const bf16x8*)(qt + arow[hf] + kk * 32);
+        da[hf] = *(const bf16x8*)(dot + arow[hf] + kk * 32);
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          s[hf][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hf], kreg[x][kk], s[hf][x], 0, 0, 0);
+          dp[hf][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[hf], vbv[x], dp[hf][x], 0, 0, 0);
+        }
     }
 
-    // P = exp2(S*scale_log2 - LSE*log2 e), dS = P (dP - delta); accumulator slot
-    // i = gq*4 + e is accumulator row m = gq*8 + hh*4 + e, query row rho(m)
-    // = 16*(gq/2) + 4e + 2*(gq&1) + hh of the tile, whose LSE and delta sit at LDS
-    // slot m.
+    // P = exp2(S*scale_log2 - LSE*log2 e), dS = P (dP - delta).  Accumulator row r
+    // of half hf is logical row 16 hf + 4 grp + r, tile row 16 hf + 2 r + goff.
     const int tq0 = t0;
     // dense problems: every query at or after q_lo sees the key (q_hi = L)
     const bool need_mask = tq0 < full_lo || (PACKED && tq0 + 32 > full_hi);
-    // Row t = tq0 + c(gq, e) + hh with c = 16*(gq/2) + 4e + 2*(gq&1) is masked when
-    // c < lo_c or c >= hi_c; outside the masked tiles the limits admit every row, so
-    // the loop has no branch and two VALU per element for the mask.
-    const int lo_c = need_mask ? q_lo - tq0 - hh : -64;
-    const int hi_c = (PACKED && need_mask) ? q_hi - tq0 - hh : 64;
-    bf16x8 pb[2], dsb[2];
+    // Tile row c + goff (c = 16 hf + 2 r) is masked for key x when c < lo_c[x] or
+    // c >= hi_c[x]; outside the masked tiles the limits admit every row.
+    int lo_c[2], hi_c[2];
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const f32x4 l4 = *(const f32x4*)(ls + gq * 8 + hh * 4);
-      const f32x4 d4 = *(const f32x4*)(dl + gq * 8 + hh * 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = gq * 4 + e;
-        const int c = 16 * (gq >> 1) + 4 * e + 2 * (gq & 1);
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.scale_log2, -l4[e] * kLog2e));
-        if (c < lo_c || (PACKED && c >= hi_c)) p = 0.0f;
-        pb[i >> 3][i & 7] = (__bf16)p;
-        dsb[i >> 3][i & 7] = (__bf16)(p * (dp[i] - d4[e]));
-      }
+    for (int x = 0; x < 2; ++x) {
+      lo_c[x] = need_mask ? q_lo[x] - tq0 - goff : -64;
+      hi_c[x] = (PACKED && need_mask) ? q_hi[x] - tq0 - goff : 64;
     }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const f32x4 l4 = *(const f32x4*)(ls + hf * 16 + grp * 4);
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s[hf][x][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hf][x][r], a.scale_log2, -l4[r]));
+    }
+    if (__builtin_expect(need_mask, 0)) {  // rare: keep it a branch
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int c = 16 * hf + 2 * r;
+            if (c < lo_c[x] || (PACKED && c >= hi_c[x])) s[hf][x][r] = 0.0f;
+          }
+    }
+    bf16x8 pb[2], dsb[2];  // [key tile]; slot 4 hf + r
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pb[x][hf * 4 + r] = (__bf16)s[hf][x][r];
+          dsb[x][hf * 4 + r] = (__bf16)(s[hf][x][r] * dp[hf][x][r]);
+        }
 
-    // dV^T += dO^T P, dK^T += Q^T dS: the A operands hold the query rows of
-    // accumulator rows mm*16 + {0..3, 8..11} + 4 hh, i.e. tile rows
-    // rho(.) = mm*16 + 4k + hh and mm*16 + 4k + 2 + hh (k = 0..3), read transposed.
+    // dV^T += dO^T P, dK^T += Q^T dS per 16-row head-dim tile: the A operands hold
+    // logical rows 4 grp + k and 16 + 4 grp + k, read transposed.
     __builtin_amdgcn_s_setprio(1);  // MFMA phase first when two waves compete for issue
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm)
+    for (int n = 0; n < NDT; ++n) {
+      const bf16x8 doa = cat(tr_read(dot + trow[0] + n * 16), tr_read(dot + trow[1] + n * 16));
+      const bf16x8 qta = cat(tr_read(qt + trow[0] + n * 16), tr_read(qt + trow[1] + n * 16));
 #pragma unroll
-      for (int n = 0; n < NDB; ++n) {
-        const int o = (mm * 16 + 4 * src_row + hh) * PS + n * 32 + src_col;
-        const bf16x8 doa = cat(tr_read(dot + o), tr_read(dot + o + 2 * PS));
-        const bf16x8 qta = cat(tr_read(qt + o), tr_read(qt + o + 2 * PS));
-        dv_t[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doa, pb[mm], dv_t[n], 0, 0, 0);
-        dk_t[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, dsb[mm], dk_t[n], 0, 0, 0);
+      for (int x = 0; x < 2; ++x) {
+        dv_t[n][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(doa, pb[x], dv_t[n][x], 0, 0, 0);
+        dk_t[n][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qta, dsb[x], dk_t[n][x], 0, 0, 0);
       }
+    }
     __builtin_amdgcn_s_setprio(0);
   };
 
   dma_xor<kKvBN, D, kKvThreads>(make_rsrc(vb, (uint32_t)L * kv_row), kv_row, u0, s_v, wave, lane);
-  dma_q(q0, do0, ls0, dl0);
+  stat_prefetch(0);
+  stat_write(ls0, dl0);
+  dma_q(q0, do0);
+  stat_prefetch(1);
   for (int it = 0; it < n_iter; it += 2) {
     step(it, q0, do0, ls0, dl0, q1, do1, ls1, dl1);
     if (it + 1 < n_iter) step(it + 1, q1, do1, ls1, dl1, q0, do0, ls0, dl0);
   }
 
-  // Add into dK and dV; accumulator rows are head-dim indices
-  // d = n*32 + (i/4)*8 + hh*4 + i%4 of this lane's key.
-  if (key_ok) {
-    const int64_t grow = (((int64_t)b * a.Hkv + g) * L + key) * D;
+  // Add into dK and dV; accumulator row r of head-dim tile n is d = 16 n + 4 grp + r
+  // of this lane's key.
 #pragma unroll
-    for (int n = 0; n < NDB; ++n)
+  for (int x = 0; x < 2; ++x) {
+    if (!key_ok[x]) continue;
+    const int64_t grow = (((int64_t)b * a.Hkv + g) * L + key[x]) * D;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        f32x4* pk = (f32x4*)(a.dk + grow + n * 32 + gq * 8 + hh * 4);
-        f32x4* pv = (f32x4*)(a.dv + grow + n * 32 + gq * 8 + hh * 4);
-        f32x4 ck = *pk, cv = *pv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ck[e] += dk_t[n][gq * 4 + e] * a.scale;
-          cv[e] += dv_t[n][gq * 4 + e];
-        }
-        *pk = ck;
-        *pv = cv;
-      }
+    for (int n = 0; n < NDT; ++n) {
+      f32x4* pk = (f32x4*)(a.dk + grow + n * 16 + grp * 4);
+      f32x4* pv = (f32x4*)(a.dv + grow + n * 16 + grp * 4);
+      *pk = *pk + dk_t[n][x] * a.scale;
+      *pv = *pv + dv_t[n][x];
+    }
   }
 }
 
