@@ -22,9 +22,9 @@
 //  * dQ kernel -- the forward's shape: one workgroup = 8 waves = 256 query rows of
 //    one (batch, query head), KV tiles of 32 keys streamed through double-buffered
 //    LDS (each tile serves all 256 rows).  Scores are computed transposed,
-//    S^T = K Q^T, so every lane holds one query row; P^T and
-//    dS^T = P^T o (dP^T - delta) feed dQ^T += K^T dS^T from registers, with K^T
-//    read by LDS transpose loads.
+//    S^T = K Q^T, on 16x16x32 MFMA tiles, so every lane holds two query rows; the
+//    dP^T accumulators start at -delta, and dS^T = P^T o (dP^T - delta) feeds
+//    dQ^T += K^T dS^T from registers, with K^T read by LDS transpose loads.
 //
 // The dQ kernel recomputes S and dP (7 MFMA passes in all instead of 5); in
 // exchange no dS exchange, no cross-workgroup reduction and no atomics remain.
@@ -70,10 +70,10 @@ __device__ inline bf16x8 cat(s16x4 a, s16x4 b) {
 //
 // LDS serves 16 lanes x 16 bytes per clock from 64 four-byte banks.
 //
-// Padded tile (read both ways): a row stride of 3 or 13 (mod 16) sixteen-byte
-// chunks is conflict free for 16-byte reads of 16 consecutive rows at one column
-// and for transpose reads of 4 consecutive rows x 32 bytes, and keeps every
-// address a per-lane base plus a compile-time offset.
+// Padded tile (read both ways): an odd row stride (3, 13 or 19 sixteen-byte chunks)
+// is conflict free for 16-byte reads of 16 rows that differ mod 16 at one column,
+// and, with the row order rho16 below, for transpose reads; it keeps every address
+// a per-lane base plus a compile-time offset.
 template <int COLS>
 struct Pad {
   static constexpr int CH = COLS / 8;
@@ -81,15 +81,6 @@ struct Pad {
   static constexpr int PS = SCH * 8;  // row stride in elements
   static constexpr int slots(int rows) { return ((rows * SCH + 63) / 64) * 64; }
 };
-
-// Row order for operands that are also read transposed.  A transpose read serves
-// 32 lanes per clock: 4 tile rows x 64 bytes.  The 4 rows of one read are the
-// accumulator rows m..m+3 of a 32x32 MFMA block; reading tile row rho(m) for
-// accumulator row m, with rho(4j + k) = 4k + j inside each 16-row block, spaces
-// those 4 rows 4 apart, and with an odd padded row stride they then fall in 16
-// distinct bank groups.  The 16-byte row reads of 16 consecutive accumulator
-// rows still touch 16 distinct rows (conflict free).
-__device__ inline int rho(int m) { return (m & ~15) | ((m & 3) << 2) | ((m >> 2) & 3); }
 
 // Swizzled tile (16-byte row reads only): XOR the chunk with the row's index among
 // the rows that share one 256-byte bank window, so 16 consecutive rows at one
@@ -482,13 +473,13 @@ constexpr int kQBN = 32;        // keys per KV tile
 
 template <int D, bool PACKED>
 __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int NKB = D / 16;
-  constexpr int ND = D / 32;
-  constexpr int NB = kQBN / 32;
+  constexpr int NKK = D / 32;  // 32-wide head-dim steps of the S^T and dP^T contractions
+  constexpr int NDT = D / 16;  // 16-row head-dim tiles of dQ^T
   using PK = Pad<D>;
   constexpr int PS = PK::PS;
   constexpr int KEL = PK::slots(kQBN) * 8;
   constexpr int VEL = kQBN * D;
+  static_assert(kQBN == 32, "one 32-key contraction step per tile");
 
   __shared__ __attribute__((aligned(16))) __bf16 k0[KEL];
   __shared__ __attribute__((aligned(16))) __bf16 k1[KEL];
@@ -497,7 +488,7 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int l32 = lane & 31, hh = lane >> 5;
+  const int l16 = lane & 15, grp = lane >> 4;
   const int L = a.map.L;
 
   const int n_qtiles = (L + kQBM - 1) / kQBM;
@@ -507,7 +498,9 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const int h = bh % a.Hq, b = bh / a.Hq;
   const int qt = n_qtiles - 1 - qi;  // heaviest (latest) query tiles first
   const int t0 = qt * kQBM;
-  const int tq = t0 + wave * 32 + l32;  // this lane's query row
+  int tq[2];  // this lane's query rows
+#pragma unroll
+  for (int x = 0; x < 2; ++x) tq[x] = t0 + wave * 32 + x * 16 + l16;
   const int g = h / a.group;
 
   const __bf16* qb = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
@@ -522,45 +515,81 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const __amdgpu_buffer_rsrc_t vr_ = make_rsrc(vb, (uint32_t)L * kv_row);
 
   // This lane's Q and dO rows: B operands of S^T = K Q^T and dP^T = V dO^T.
-  bf16x8 qr[NKB], dr[NKB];
+  bf16x8 qr[2][NKK], dr[2][NKK];
+  float lse2[2], dlt[2];
 #pragma unroll
-  for (int kk = 0; kk < NKB; ++kk) {
-    qr[kk] = load_row8(qr_, (uint32_t)tq * q_row + (uint32_t)(kk * 32 + hh * 16));
-    dr[kk] = load_row8(or_, (uint32_t)tq * o_row + (uint32_t)(kk * 32 + hh * 16));
+  for (int x = 0; x < 2; ++x) {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      qr[x][kk] = load_row8(qr_, (uint32_t)tq[x] * q_row + (uint32_t)(kk * 64 + grp * 16));
+      dr[x][kk] = load_row8(or_, (uint32_t)tq[x] * o_row + (uint32_t)(kk * 64 + grp * 16));
+    }
+    const int64_t row = ((int64_t)b * a.Hq + h) * L + tq[x];
+    lse2[x] = tq[x] < L ? a.lse[row] * kLog2e : 0.0f;
+    dlt[x] = tq[x] < L ? a.delta[row] : 0.0f;
   }
-  const int64_t row = ((int64_t)b * a.Hq + h) * L + tq;
-  const float lse2 = tq < L ? a.lse[row] * kLog2e : 0.0f;
-  const float dlt = tq < L ? a.delta[row] : 0.0f;
+  // -delta of each row, the start of the dP^T accumulators (they then hold dP^T - delta)
+  f32x4 ndlt[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) ndlt[x] = f32x4{-dlt[x], -dlt[x], -dlt[x], -dlt[x]};
 
-  // Visible keys of this row and of the workgroup (as in the forward): key tiles
+  // Visible keys of each row and of the workgroup (as in the forward): key tiles
   // j0..n_tiles-1, no mask inside [full_lo, n_full).
-  int kv_lo = 0, kv_lim = L, j0 = 0, n_keys = L, full_lo = 0, n_full = L;
+  int kv_lo[2] = {0, 0}, kv_lim[2] = {L, L};
+  int j0 = 0, n_keys = L, full_lo = 0, n_full = L;
   if constexpr (PACKED) {  // packed documents
     __shared__ int red[4];
-    if (tq < L) {
-      key_interval(a.map, a.ck, pos_of(a.map, a.cq, tq), a.causal, a.seg + (int64_t)b * a.seg_n,
-                   a.seg_n, kv_lo, kv_lim);
-    } else {
-      kv_lo = L;
-      kv_lim = 0;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      if (tq[x] < L) {
+        key_interval(a.map, a.ck, pos_of(a.map, a.cq, tq[x]), a.causal,
+                     a.seg + (int64_t)b * a.seg_n, a.seg_n, kv_lo[x], kv_lim[x]);
+      } else {
+        kv_lo[x] = L;
+        kv_lim[x] = 0;
+      }
     }
-    int min_lo;
-    wg_interval_reduce(red, kv_lo, kv_lim, L, min_lo, n_keys, full_lo, n_full);
-    j0 = min_lo / kQBN;
+    if (tid == 0) {
+      red[0] = L;
+      red[1] = 0;
+      red[2] = 0;
+      red[3] = L;
+    }
+    __syncthreads();
+    atomicMin(&red[0], min(kv_lo[0], kv_lo[1]));
+    atomicMax(&red[1], max(kv_lim[0], kv_lim[1]));
+    atomicMax(&red[2], max(kv_lo[0], kv_lo[1]));
+    atomicMin(&red[3], min(kv_lim[0], kv_lim[1]));
+    __syncthreads();
+    j0 = red[0] / kQBN;
+    n_keys = red[1];
+    full_lo = red[2];
+    n_full = red[3];
   } else if (a.causal) {
     const int t_last = min(t0 + kQBM, L) - 1;
-    kv_lim = count_le(a.map, a.ck, pos_of(a.map, a.cq, min(tq, L - 1)));
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      kv_lim[x] = count_le(a.map, a.ck, pos_of(a.map, a.cq, min(tq[x], L - 1)));
     n_keys = count_le(a.map, a.ck, pos_of(a.map, a.cq, t_last));
     n_full = count_le(a.map, a.ck, pos_of(a.map, a.cq, t0));
   }
   const int n_tiles = (n_keys + kQBN - 1) / kQBN;
 
-  f32x16 dq_t[ND];
+  f32x4 dq_t[NDT][2];  // [head-dim tile][query half]
 #pragma unroll
-  for (int n = 0; n < ND; ++n) dq_t[n] = f32x16{};
+  for (int n = 0; n < NDT; ++n) dq_t[n][0] = dq_t[n][1] = f32x4{};
 
-  const int src_row = (lane & 15) >> 2;
-  const int src_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  // Logical key l of a tile lives in tile row rho16(l) (K and V alike).  A-operand
+  // rows of S^T and dP^T: logical keys 16 t + l16; transpose-read sources of K^T:
+  // logical keys 16 hf + 4 grp + l16 / 4, columns 4 (l16 % 4) of a 16-column tile.
+  int krow[2], trow[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    krow[t] = rho16(t * 16 + l16);
+    trow[t] = rho16(t * 16 + grp * 4 + (l16 >> 2)) * PS + (l16 & 3) * 4;
+  }
+  // Key of accumulator row r of key tile t: u0 + 16 t + 2 r + goff.
+  const int goff = 8 * (grp & 1) + (grp >> 1);
 
   auto dma_kv = [&](int j, __bf16* kn, __bf16* vn) {
     dma_pad<kQBN, D, kQThreads>(kr_, kv_row, j * kQBN, kn, wave, lane);
@@ -572,65 +601,67 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     __syncthreads();                     // every wave's; tile j-1 is free
     if (j + 1 < n_tiles) dma_kv(j + 1, kn, vn);
 
-    // S^T and dP^T for this tile: NB blocks of 32 keys x 32 queries; accumulator
-    // row m of block blk is key blk*32 + rho(m) of the tile.
-    f32x16 s[NB], dp[NB];
+    // S^T and dP^T - delta for this tile: [key tile][query half] 16x16 blocks.
+    f32x4 s[2][2], dp[2][2];
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
-      s[blk] = f32x16{};
-      dp[blk] = f32x16{};
-    }
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int kk = 0; kk < NKB; ++kk)
+      for (int x = 0; x < 2; ++x) {
+        s[t][x] = f32x4{};
+        dp[t][x] = ndlt[x];
+      }
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        const int r = blk * 32 + rho(l32), col = kk * 16 + hh * 8;
-        const bf16x8 ka = *(const bf16x8*)(kt + r * PS + col);
-        const bf16x8 va = *(const bf16x8*)(vt + xoff<D>(r, col));
-        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qr[kk], s[blk], 0, 0, 0);
-        dp[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dr[kk], dp[blk], 0, 0, 0);
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 ka = *(const bf16x8*)(kt + krow[t] * PS + kk * 32 + grp * 8);
+        const bf16x8 va = *(const bf16x8*)(vt + xoff<D>(krow[t], kk * 32 + grp * 8));
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          s[t][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qr[x][kk], s[t][x], 0, 0, 0);
+          dp[t][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, dr[x][kk], dp[t][x], 0, 0, 0);
+        }
       }
 
-    // P^T = exp2(S^T*scale_log2 - LSE*log2 e) with keys past the row's visible
-    // prefix masked; dS^T = P^T (dP^T - delta).
+    // P^T = exp2(S^T*scale_log2 - LSE*log2 e) with keys outside the row's visible
+    // interval masked; dS^T = P^T (dP^T - delta).
     const int u0 = j * kQBN;
     const bool need_mask = u0 < full_lo || u0 + kQBN > n_full;
-    float pv[NB][16];
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        pv[blk][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][i], a.scale_log2, -lse2));
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s[t][x][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][x][r], a.scale_log2, -lse2[x]));
     if (__builtin_expect(need_mask, 0)) {  // rare: keep it a branch
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          // accumulator row m = (i/4)*8 + hh*4 + i%4, key rho(m)
-          const int u = u0 + blk * 32 + 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1) + hh;
-          if (u < kv_lo || u >= kv_lim) pv[blk][i] = 0.0f;
-        }
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int u = u0 + 16 * t + 2 * r + goff;
+            if (u < kv_lo[x] || u >= kv_lim[x]) s[t][x][r] = 0.0f;
+          }
     }
-    bf16x8 dsb[NB][2];
+    bf16x8 dsb[2];  // [query half]; slot 4 t + r holds logical key 16 t + 4 grp + r
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        dsb[blk][i >> 3][i & 7] = (__bf16)(pv[blk][i] * (dp[blk][i] - dlt));
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          dsb[x][t * 4 + r] = (__bf16)(s[t][x][r] * dp[t][x][r]);
 
-    // dQ^T += K^T dS^T: the A operand of block (blk, mm) holds the keys of
-    // accumulator rows mm*16 + {0..3, 8..11} + 4 hh, i.e. tile rows
-    // blk*32 + mm*16 + 4k + hh and + 2 (k = 0..3), read transposed from the K tile.
+    // dQ^T += K^T dS^T per 16-row head-dim tile; K^T read transposed.
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk)
+    for (int n = 0; n < NDT; ++n) {
+      const bf16x8 kta = cat(tr_read(kt + trow[0] + n * 16), tr_read(kt + trow[1] + n * 16));
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-        for (int n = 0; n < ND; ++n) {
-          const int o = (blk * 32 + mm * 16 + 4 * src_row + hh) * PS + n * 32 + src_col;
-          const bf16x8 kta = cat(tr_read(kt + o), tr_read(kt + o + 2 * PS));
-          dq_t[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta, dsb[blk][mm], dq_t[n], 0, 0, 0);
-        }
+      for (int x = 0; x < 2; ++x)
+        dq_t[n][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kta, dsb[x], dq_t[n][x], 0, 0, 0);
+    }
   };
 
   if (n_tiles > j0) dma_kv(j0, k0, v0);
@@ -639,19 +670,18 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     if (j + 1 < n_tiles) tile(j + 1, k1, v1, k0, v0);
   }
 
-  // dQ[q][d] += scale * dQ^T[d][q]; accumulator rows are d = n*32 + (i/4)*8 + hh*4 + i%4.
-  if (tq < L && n_tiles > j0) {
-    float* dqr = a.dq + row * D;
+  // dQ[q][d] += scale * dQ^T[d][q]; accumulator row r of tile n is d = 16 n + 4 grp + r.
+  if (n_tiles > j0) {
 #pragma unroll
-    for (int n = 0; n < ND; ++n)
+    for (int x = 0; x < 2; ++x) {
+      if (tq[x] >= L) continue;
+      float* dqr = a.dq + (((int64_t)b * a.Hq + h) * L + tq[x]) * D;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        f32x4* p = (f32x4*)(dqr + n * 32 + gq * 8 + hh * 4);
-        f32x4 c = *p;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) c[e] += dq_t[n][gq * 4 + e] * a.scale;
-        *p = c;
+      for (int n = 0; n < NDT; ++n) {
+        f32x4* p = (f32x4*)(dqr + n * 16 + grp * 4);
+        *p = *p + dq_t[n][x] * a.scale;
       }
+    }
   }
 }
 
