@@ -216,7 +216,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, Bf16Cfg<D>::NW == 8 ? 1 : 2) void f
   constexpr int NKB = D / 16;  // 16-wide head-dim blocks of the QK^T contraction
   constexpr int ND = D / 32;   // 32-row head-dim blocks of O^T
   constexpr int NB = BN / 32;  // 32-key blocks per tile
-  constexpr float kRescale = 8.0f;  // lazy rescale threshold (log2 units): p <= 2^8
+  constexpr float kSumCap = 256.0f;  // lazy rescale bound on a lane's partial sum: p <= 2^8
   // Two distinct LDS objects per tensor (not one indexed array): the compiler can
   // then prove that the loads into one buffer never alias the reads of the other
   // and does not wait for the prefetch before computing on the current tile.
@@ -326,35 +326,42 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, Bf16Cfg<D>::NW == 8 ? 1 : 2) void f
         }
     }
 
-    // Online softmax with lazy rescaling: the reference max only moves when the
-    // tile's max exceeds it by more than 2^kRescale in probability, so p <= 2^8.
-    float mx = kNegInf;
+    // Online softmax with a lazily moved reference max.  P is first taken against
+    // the current reference; every p is at most its lane's partial row sum, so
+    // while each partial stays <= 2^8 no p exceeds 2^8 and the reference may stay.
+    // Otherwise (the first visible tile, or a row whose max rose) the wave finds
+    // the exact row max, rescales O and l, and takes P again.
+    bf16x8 pb[NB][2];
+    auto expo = [&](float mc) {
+      float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four short chains instead of one
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk)
+      for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[blk][i]);
-    mx = pair_max(mx);
-    const bool grow = (mx - st.m) * a.scale_log2 > kRescale;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = grow ? mx : st.m;
+        for (int i = 0; i < 16; ++i) {
+          const float pv = fast_exp2(__builtin_fmaf(s[blk][i], a.scale_log2, -mc));
+          lsum[i & 3] += pv;
+          pb[blk][i >> 3][i & 7] = (__bf16)pv;
+        }
+      return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    };
+    float part = expo(st.m * a.scale_log2);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(part <= kSumCap)) != 0, 0)) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[blk][i]);
+      mx = pair_max(mx);
+      const bool reset = !(pair_max(part) <= kSumCap);
+      const float m_new = reset ? fmaxf(mx, st.m) : st.m;
       const float alpha = fast_exp2((st.m - m_new) * a.scale_log2);
       st.m = m_new;
       st.l *= alpha;
 #pragma unroll
       for (int n = 0; n < ND; ++n) o_t[n] *= alpha;
+      part = expo(st.m * a.scale_log2);
     }
-    const float mc = st.m * a.scale_log2;
-    float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four short chains instead of one long one
-    bf16x8 pb[NB][2];
-#pragma unroll
-    for (int blk = 0; blk < NB; ++blk)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(__builtin_fmaf(s[blk][i], a.scale_log2, -mc));
-        lsum[i & 3] += pv;
-        pb[blk][i >> 3][i & 7] = (__bf16)pv;
-      }
-    st.l += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    st.l += part;
 
     // O^T += V^T P^T.  The A operand of block (blk, mm) holds keys
     // blk*32 + mm*16 + {0..3, 8..11} + 4 hh, read with two transpose loads.
