@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from ring_context_parallelism_amd import ra, staging
-from ring_context_parallelism_amd.workloads import WORKLOADS, Workload, generate
+from ring_context_parallelism_amd.workloads import WORKLOADS, Workload, generate, round_bf16
 from tests.gpu_util import assert_close, assert_lse, need_gpu, sample_heads, sample_rows, say
 
 pytestmark = pytest.mark.gpu
@@ -66,6 +66,50 @@ def test_ring_fwd_every_rank(w):
         got = _np(out)
         assert_close(got[..., :d], O, w.dtype, f"O rank {r}")
         assert np.all(got[..., d:] == 0.0), "padded head-dim columns must stay exactly 0"
+        assert_lse(_np(lse), LSE, f"LSE rank {r}")
+
+
+# Scores that keep growing along the key axis, plus one outlier key: the running max of
+# every row moves on most tiles, so the rescaling path of the online softmax runs over
+# and over (random inputs settle the max on the first tile).
+MOVING_MAX = [
+    _wl("bf16", 128, 128, "contiguous", 2, 1100, True, 1, 2, 1, seed=120),
+    _wl("bf16", 64, 64, "zigzag", 2, 1040, False, 1, 2, 2, seed=121),
+    _wl("bf16", 32, 24, "striped", 2, 1000, True, 1, 2, 1, dist="uniform", scale=1.0, seed=122),
+    _wl("f32", 64, 64, "striped", 2, 1024, True, 1, 1, 1, seed=123),
+]
+
+
+def _moving_max_inputs(w):
+    """q_i + 1 in every component and k_j + beta_j / sqrt(d): s_ij grows by about beta_j,
+    with beta ramping 0 -> 40 along the sequence and one key at S/2 + 3 raised by 60."""
+    arrays = generate(w)
+    S, d = w.seq_total, w.head_dim
+    beta = np.linspace(0.0, 40.0, S, dtype=np.float32)
+    beta[S // 2 + 3] += 60.0
+    q = arrays["q"] + 1.0
+    k = arrays["k"] + (beta / np.sqrt(d))[None, None, :, None]
+    if w.dtype == "bf16":
+        q, k = round_bf16(q), round_bf16(k)
+    arrays["q"], arrays["k"] = q.astype(np.float32), k.astype(np.float32)
+    return arrays
+
+
+@pytest.mark.parametrize("w", MOVING_MAX, ids=_ids)
+def test_ring_fwd_moving_max(w):
+    dev = need_gpu()
+    arrays = _moving_max_inputs(w)
+    d = w.head_dim
+    for r in range(w.world):
+        say(f"moving max {_ids(w)} rank {r}")
+        share = staging.stage(w, arrays, dev, rank=r)
+        out, lse = staging.ring_forward(share, w, rank=r)
+        torch.cuda.synchronize()
+        rows = oracle.positions(w.layout, w.seq_total, w.world, r)
+        O, LSE = oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal)
+        assert LSE.max() - LSE.min() > 15.0, "the inputs must move the row maxima"
+        got = _np(out)
+        assert_close(got[..., :d], O, w.dtype, f"O rank {r}")
         assert_lse(_np(lse), LSE, f"LSE rank {r}")
 
 
