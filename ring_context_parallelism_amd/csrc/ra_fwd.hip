@@ -12,14 +12,14 @@
 //  * one workgroup = 4 or 8 waves = BM = 128 or 256 query rows of one (batch,
 //    query head) (8 at head dim 128); each wave owns 32 query rows;
 //  * the KV chunk is streamed in tiles of BN keys through double-buffered LDS;
-//  * scores are computed transposed, S^T = K Q^T, with 32x32 MFMA tiles, so that in
-//    the accumulator layout every lane holds one query row (column l % 32) and
-//    half of that row's keys; the other half sits in lane l ^ 32.  The softmax
-//    statistics are therefore per-lane scalars and a row max needs one exchange;
-//  * P^T (rounded to bf16) is used directly from registers as the B operand of the
-//    PV MFMA O^T += V^T P^T; V is written transposed into LDS with a key permutation
-//    that matches the accumulator's key order, so each lane's 8 keys are one 16-byte
-//    LDS read;
+//  * bf16: scores are computed transposed, S^T = K Q^T, with 16x16x32 MFMA tiles;
+//    every lane holds two query rows and a quarter of their keys, so the softmax
+//    statistics are per-lane and row reductions take two lane exchanges.  P^T
+//    (rounded to bf16) is the B operand of the PV MFMA O^T += V^T P^T straight
+//    from registers, and V^T comes from LDS transpose loads;
+//  * the reference max of the online softmax moves lazily: P is taken against the
+//    current reference, and only when a lane's partial row sum of a tile exceeds
+//    2^8 does the wave find the exact row max and rescale (so p <= 2^8 always);
 //  * fp32 problems use the fp32 32x32x2 MFMA with K and V row-major in LDS.
 #include "ra_internal.h"
 
@@ -171,31 +171,40 @@ struct Bf16Tile {
 // chunk with the row's window index spreads those rows over all 16 bank groups.
 template <int D>
 __device__ inline int k_swz(int r) { return (r / Bf16Tile<D>::RPW) & (Bf16Tile<D>::KCH - 1); }
-// V tile: a transpose read serves 32 lanes per clock, 4 consecutive rows x 64
-// bytes (4 chunks).  With 16 chunks per row (D = 128) the rows need chunk XORs
-// 4 apart, ((r & 3) << 2), so the 4 rows x 4 chunks hit 16 distinct bank groups;
-// adding (r >> 2) & 3 in the low bits, which differs between the two 32-lane
-// halves of a read, measured faster still (~179 against ~164 B/clk).  With 8 chunks
-// per row two rows share a 256-byte bank window and ((r & 3) << 1) suffices; with
-// 4 chunks 4 consecutive rows are one window.
+// The bf16 kernel uses 16x16x32 MFMA tiles: on this chip a stream of them sustains
+// about 15% more FLOP/s than 32x32x16 tiles under the board power limit.
+// Accumulator layout of a 16x16 tile: lane l holds column l % 16 and rows
+// 4 (l / 16) + r, r = 0..3; operands hold row (A) or column (B) l % 16 and the 8
+// contraction indices 8 (l / 16) + j.
+//  * S^T = K Q^T per 16-key x 16-query tile: each lane holds two query rows
+//    (l % 16 and 16 + l % 16 of the wave's 32) and 4 keys of every 16-key tile; a
+//    row's keys are spread over the four 16-lane groups.
+//  * P^T feeds O^T += V^T P^T from registers: contraction slot 8 g + j of a 32-key
+//    step holds key 4 g + j (j < 4) or 16 + 4 g + j - 4, which is what the
+//    accumulators of the step's two key tiles give lane group g; V^T is read with
+//    two transpose loads of 4 keys each.
+
+// V tile swizzle for this access: one transpose read serves two 16-lane groups per
+// clock, rows 4g..4g+7 at one 32-byte column pair; the chunk XOR puts those 8 rows x
+// 2 chunks in 16 distinct bank groups.
 template <int D>
 __device__ inline int v_swz(int r) {
-  if constexpr (Bf16Tile<D>::KCH >= 16) return ((r & 3) << 2) | ((r >> 2) & 3);
-  return Bf16Tile<D>::KCH >= 8 ? ((r & 3) << 1) : (((r >> 1) & 1) << 1);
+  if constexpr (Bf16Tile<D>::KCH >= 16) return ((r & 3) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+  if constexpr (Bf16Tile<D>::KCH == 8) return ((r >> 1) & 3) << 1;
+  return ((r >> 2) & 1) << 1;
 }
 
-// Issues the direct-to-LDS loads of one BN x D tile (rows u0..u0+BN-1) of K and V.
 template <int D, int BN, int NT>
 __device__ inline void dma_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
-                                uint32_t row_bytes, int u0, __bf16* ks, __bf16* vs, int wave,
-                                int lane) {
+                                  uint32_t row_bytes, int u0, __bf16* ks, __bf16* vs, int wave,
+                                  int lane) {
   constexpr int KCH = Bf16Tile<D>::KCH;
-  constexpr int SLOTS = BN * KCH;                  // 16-byte slots per tile
-  constexpr int NI = SLOTS / NT;                   // loads per thread per tensor
+  constexpr int SLOTS = BN * KCH;
+  constexpr int NI = SLOTS / NT;
   static_assert(SLOTS % NT == 0, "tile must be a whole number of workgroup loads");
 #pragma unroll
   for (int it = 0; it < NI; ++it) {
-    const int base = it * NT + wave * 64;          // first slot of this wave's load
+    const int base = it * NT + wave * 64;
     const int slot = base + lane;
     const int r = slot / KCH, pc = slot % KCH;
     const uint32_t roff = (uint32_t)(u0 + r) * row_bytes;
@@ -206,28 +215,88 @@ __device__ inline void dma_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_
   }
 }
 
-// PK: packed documents (a.seg != nullptr).  A separate instantiation, so the
-// dense kernel carries none of the packed path's registers.
+// Max and sum over the four 16-lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48), which
+// hold the same query rows.
+__device__ inline float quad_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return pair_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ inline float quad_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return pair_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+// Epilogue of one query row in the 16x16 layout: o[dt] holds O^T[d][q] for
+// d = 16 dt + 4 grp + r.
+template <int D>
+__device__ inline void fwd_epilogue16(const FwdArgs& a, int b, int h, int tq, int grp, float m,
+                                      float l, const f32x4 (&o)[D / 16]) {
+  const int L = a.map.L;
+  const float l_tot = quad_sum(l);
+  const bool live = l_tot > 0.0f;
+  const float lse_s = live ? (m * a.scale_log2 + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
+  const float inv_l = live ? 1.0f / l_tot : 0.0f;
+  if (tq >= L) return;
+  const int64_t row = ((int64_t)b * a.Hq + h) * L + tq;
+  float w_acc = 0.0f, w_s = inv_l, lse_new = lse_s;
+  if (a.acc_in != nullptr) {
+    const float lse_a = a.lse_in[row];
+    if (!live) {
+      w_acc = 1.0f;
+      w_s = 0.0f;
+      lse_new = lse_a;
+    } else if (lse_a == kNegInf) {
+      w_acc = 0.0f;
+    } else {
+      const float mx = fmaxf(lse_a, lse_s);
+      const float ea = __expf(lse_a - mx), es = __expf(lse_s - mx);
+      const float den = ea + es;
+      lse_new = mx + __logf(den);
+      w_acc = ea / den;
+      w_s = es / den * inv_l;
+    }
+  }
+  const float* acc = a.acc_in ? a.acc_in + row * D : nullptr;
+  char* obase = (char*)a.out;
+  const int64_t orow = (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)tq * a.o_st;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const int d0 = dt * 16 + grp * 4;
+    f32x4 v = o[dt] * w_s;
+    if (acc != nullptr && w_acc != 0.0f) v += *(const f32x4*)(acc + d0) * w_acc;
+    if (a.out_f32) {
+      *(f32x4*)(obase + (orow + d0) * 4) = v;
+    } else {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 w;
+      w[0] = (__bf16)v[0];
+      w[1] = (__bf16)v[1];
+      w[2] = (__bf16)v[2];
+      w[3] = (__bf16)v[3];
+      *(bf16x4*)(obase + (orow + d0) * 2) = w;
+    }
+  }
+  if (grp == 0) a.lse_out[row] = lse_new;
+}
+
 template <int D, int BN, bool PK>
 __global__ __launch_bounds__(Bf16Cfg<D>::NT, Bf16Cfg<D>::NW == 8 ? 1 : 2) void fwd_bf16_kernel(
     FwdArgs a) {
-  constexpr int kBM = Bf16Cfg<D>::BM;  // query rows per workgroup
+  constexpr int kBM = Bf16Cfg<D>::BM;
   constexpr int NT = Bf16Cfg<D>::NT;
-  constexpr int NKB = D / 16;  // 16-wide head-dim blocks of the QK^T contraction
-  constexpr int ND = D / 32;   // 32-row head-dim blocks of O^T
-  constexpr int NB = BN / 32;  // 32-key blocks per tile
+  constexpr int NKK = D / 32;   // 32-wide head-dim steps of the QK^T contraction
+  constexpr int NDT = D / 16;   // 16-row head-dim tiles of O^T
+  constexpr int NKT = BN / 16;  // 16-key tiles per KV tile
+  constexpr int NC = BN / 32;   // 32-key steps of the PV contraction
   constexpr float kSumCap = 256.0f;  // lazy rescale bound on a lane's partial sum: p <= 2^8
-  // Two distinct LDS objects per tensor (not one indexed array): the compiler can
-  // then prove that the loads into one buffer never alias the reads of the other
-  // and does not wait for the prefetch before computing on the current tile.
   __shared__ __attribute__((aligned(16))) __bf16 ks0[BN * D];
   __shared__ __attribute__((aligned(16))) __bf16 ks1[BN * D];
   __shared__ __attribute__((aligned(16))) __bf16 vs0[BN * D];
   __shared__ __attribute__((aligned(16))) __bf16 vs1[BN * D];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, grp = lane >> 4;
   const int L = a.map.L;
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -236,7 +305,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, Bf16Cfg<D>::NW == 8 ? 1 : 2) void f
   const int h = bh % a.Hq, b = bh / a.Hq;
   const int qt = a.n_qtiles - 1 - qi;  // heaviest (latest) query tiles first
   const int t0 = qt * kBM;
-  const int tq = t0 + wave * 32 + l32;
+  const int tq[2] = {t0 + wave * 32 + l16, t0 + wave * 32 + 16 + l16};
   const int g = h / a.group;
 
   const __bf16* qb = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
@@ -247,145 +316,166 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, Bf16Cfg<D>::NW == 8 ? 1 : 2) void f
   const __amdgpu_buffer_rsrc_t kr_ = make_rsrc(kb, (uint32_t)L * kv_row);
   const __amdgpu_buffer_rsrc_t vr_ = make_rsrc(vb, (uint32_t)L * kv_row);
 
-  // This lane's query row as the B operand of S^T = K Q^T (rows >= L read as 0).
-  bf16x8 qr[NKB];
+  // The two query rows of this lane as B operands of S^T = K Q^T (rows >= L read 0).
+  bf16x8 qr[2][NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKB; ++kk) {
-    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
-        qr_, (uint32_t)tq * q_row + (uint32_t)(kk * 32 + hh * 16), 0, 0);
-    qr[kk] = __builtin_bit_cast(bf16x8, w);
-  }
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qr[x][kk] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                      qr_, (uint32_t)tq[x] * q_row + (uint32_t)(kk * 64 + grp * 16), 0, 0));
 
-  // Visible keys [kv_lo, kv_lim) of this row; key tiles j0..n_tiles-1 hold those of
+  // Visible keys [kv_lo, kv_lim) of each row; key tiles j0..n_tiles-1 hold those of
   // every row, and [full_lo, n_full) is visible to every row (no mask).
-  int kv_lo = 0, kv_lim = L, j0 = 0, n_keys = L, full_lo = 0, n_full = L;
-  if constexpr (PK) {  // packed documents
+  int kv_lo[2] = {0, 0}, kv_lim[2] = {L, L};
+  int j0 = 0, n_keys = L, full_lo = 0, n_full = L;
+  if constexpr (PK) {
     __shared__ int red[4];
-    if (tq < L) {
-      key_interval(a.map, a.ck, pos_of(a.map, a.cq, tq), a.causal, a.seg + (int64_t)b * a.seg_n,
-                   a.seg_n, kv_lo, kv_lim);
-    } else {
-      kv_lo = L;
-      kv_lim = 0;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      if (tq[x] < L) {
+        key_interval(a.map, a.ck, pos_of(a.map, a.cq, tq[x]), a.causal,
+                     a.seg + (int64_t)b * a.seg_n, a.seg_n, kv_lo[x], kv_lim[x]);
+      } else {
+        kv_lo[x] = L;
+        kv_lim[x] = 0;
+      }
     }
-    int min_lo;
-    wg_interval_reduce(red, kv_lo, kv_lim, L, min_lo, n_keys, full_lo, n_full);
-    j0 = min_lo / BN;
-  } else if (a.causal) {  // dense: the visible keys are a prefix, monotone in the row
+    if (tid == 0) {
+      red[0] = L;
+      red[1] = 0;
+      red[2] = 0;
+      red[3] = L;
+    }
+    __syncthreads();
+    atomicMin(&red[0], min(kv_lo[0], kv_lo[1]));
+    atomicMax(&red[1], max(kv_lim[0], kv_lim[1]));
+    atomicMax(&red[2], max(kv_lo[0], kv_lo[1]));
+    atomicMin(&red[3], min(kv_lim[0], kv_lim[1]));
+    __syncthreads();
+    j0 = red[0] / BN;
+    n_keys = red[1];
+    full_lo = red[2];
+    n_full = red[3];
+  } else if (a.causal) {
     const int t_last = min(t0 + kBM, L) - 1;
-    kv_lim = count_le(a.map, a.ck, pos_of(a.map, a.cq, min(tq, L - 1)));
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      kv_lim[x] = count_le(a.map, a.ck, pos_of(a.map, a.cq, min(tq[x], L - 1)));
     n_keys = count_le(a.map, a.ck, pos_of(a.map, a.cq, t_last));
     n_full = count_le(a.map, a.ck, pos_of(a.map, a.cq, t0));
   }
   const int n_tiles = (n_keys + BN - 1) / BN;
 
-  RowState st{kMInit, 0.0f};
-  f32x16 o_t[ND];
+  float m[2] = {kMInit, kMInit}, l[2] = {0.0f, 0.0f};
+  f32x4 o[NDT][2];
 #pragma unroll
-  for (int n = 0; n < ND; ++n) o_t[n] = f32x16{};
+  for (int dt = 0; dt < NDT; ++dt) o[dt][0] = o[dt][1] = f32x4{};
 
   if (n_tiles > j0) dma_tile<D, BN, NT>(kr_, vr_, kv_row, j0 * BN, ks0, vs0, wave, lane);
 
-  // Transpose-read geometry: source lane s of each 16-lane group points at key row
-  // (s / 4) of a 4-row block and head-dim column 4 (s % 4) of the lane group's 16
-  // columns; lane j then receives 4 consecutive keys at column j.
-  const int src_row = (lane & 15) >> 2;
-  const int src_col = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  // Transpose-read source of this lane: row l16 / 4 of its group's 4-row block,
+  // columns 4 (l16 % 4) of the 16-column tile.
+  const int src_row = l16 >> 2;
+  const int src_col = (l16 & 3) * 4;
 
-  // One tile: wait for its loads, start the next tile's loads into the other
-  // buffer, then QK^T, softmax and PV on this one.
   auto tile = [&](int j, const __bf16* kt, const __bf16* vt, __bf16* kn, __bf16* vn) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile j landed
     __syncthreads();                     // ... and every other wave's; tile j-1 is free
     if (j + 1 < n_tiles) dma_tile<D, BN, NT>(kr_, vr_, kv_row, (j + 1) * BN, kn, vn, wave, lane);
-    __builtin_amdgcn_iglp_opt(0);  // scheduling hint: interleave LDS reads with MFMAs
+    __builtin_amdgcn_iglp_opt(0);
 
-    // S^T for this tile: NB blocks of 32 keys x 32 queries.
-    f32x16 s[NB];
+    f32x4 s[NKT][2];
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) s[blk] = f32x16{};
+    for (int t = 0; t < NKT; ++t) s[t][0] = s[t][1] = f32x4{};
 #pragma unroll
-    for (int kk = 0; kk < NKB; ++kk)
+    for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        const int r = blk * 32 + l32;
-        const bf16x8 kop = *(const bf16x8*)(kt + r * D + (((kk * 2 + hh) ^ k_swz<D>(r)) << 3));
-        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qr[kk], s[blk], 0, 0, 0);
+      for (int t = 0; t < NKT; ++t) {
+        const int r = t * 16 + l16;
+        const bf16x8 kop = *(const bf16x8*)(kt + r * D + (((kk * 4 + grp) ^ k_swz<D>(r)) << 3));
+        s[t][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qr[0][kk], s[t][0], 0, 0, 0);
+        s[t][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qr[1][kk], s[t][1], 0, 0, 0);
       }
 
-    // Mask keys outside this row's visible interval (causal diagonal, document
-    // edges, ragged tail).
     const int u0 = j * BN;
-    if (u0 < full_lo || u0 + BN > n_full) {
+    if (__builtin_expect(u0 < full_lo || u0 + BN > n_full, 0)) {  // rare: keep it a branch
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk)
+      for (int t = 0; t < NKT; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int u = u0 + blk * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-          if (u < kv_lo || u >= kv_lim) s[blk][i] = kNegInf;
-        }
-    }
-
-    // Online softmax with a lazily moved reference max.  P is first taken against
-    // the current reference; every p is at most its lane's partial row sum, so
-    // while each partial stays <= 2^8 no p exceeds 2^8 and the reference may stay.
-    // Otherwise (the first visible tile, or a row whose max rose) the wave finds
-    // the exact row max, rescales O and l, and takes P again.
-    bf16x8 pb[NB][2];
-    auto expo = [&](float mc) {
-      float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four short chains instead of one
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = fast_exp2(__builtin_fmaf(s[blk][i], a.scale_log2, -mc));
-          lsum[i & 3] += pv;
-          pb[blk][i >> 3][i & 7] = (__bf16)pv;
-        }
-      return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
-    };
-    float part = expo(st.m * a.scale_log2);
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(part <= kSumCap)) != 0, 0)) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int blk = 0; blk < NB; ++blk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[blk][i]);
-      mx = pair_max(mx);
-      const bool reset = !(pair_max(part) <= kSumCap);
-      const float m_new = reset ? fmaxf(mx, st.m) : st.m;
-      const float alpha = fast_exp2((st.m - m_new) * a.scale_log2);
-      st.m = m_new;
-      st.l *= alpha;
-#pragma unroll
-      for (int n = 0; n < ND; ++n) o_t[n] *= alpha;
-      part = expo(st.m * a.scale_log2);
-    }
-    st.l += part;
-
-    // O^T += V^T P^T.  The A operand of block (blk, mm) holds keys
-    // blk*32 + mm*16 + {0..3, 8..11} + 4 hh, read with two transpose loads.
-#pragma unroll
-    for (int blk = 0; blk < NB; ++blk)
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        bf16x8 vop[ND];
-#pragma unroll
-        for (int n = 0; n < ND; ++n) {
-          s16x4 x[2];
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int r = blk * 32 + mm * 16 + half * 8 + hh * 4 + src_row;
-            const int col = n * 32 + src_col;
-            const __bf16* ptr = vt + r * D + ((((col >> 3) ^ v_swz<D>(r))) << 3) + (col & 7);
-            x[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)ptr);
+          for (int r = 0; r < 4; ++r) {
+            const int u = u0 + t * 16 + grp * 4 + r;
+            if (u < kv_lo[x] || u >= kv_lim[x]) s[t][x][r] = kNegInf;
           }
-          vop[n] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        }
+    }
+
+    bf16x8 pb[2][NC];
+    auto expo = [&](int x) {
+      const float mc = m[x] * a.scale_log2;
+      float ls[2] = {0.0f, 0.0f};
 #pragma unroll
-        for (int n = 0; n < ND; ++n)
-          o_t[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[n], pb[blk][mm], o_t[n], 0, 0, 0);
+      for (int t = 0; t < NKT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pv = fast_exp2(__builtin_fmaf(s[t][x][r], a.scale_log2, -mc));
+          ls[r & 1] += pv;
+          pb[x][t >> 1][(t & 1) * 4 + r] = (__bf16)pv;
+        }
+      return ls[0] + ls[1];
+    };
+    // P against the current reference max first; every p is at most its lane's
+    // partial row sum, so while the partials stay <= 2^8 the reference may stay.
+    // Otherwise (the first visible tile, or a row whose max rose) the wave finds the
+    // exact row max, rescales O and l, and takes P again.
+    float part[2] = {expo(0), expo(1)};
+    if (__builtin_expect(
+            __builtin_amdgcn_ballot_w64(!(part[0] <= kSumCap && part[1] <= kSumCap)) != 0, 0)) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        float v = kNegInf;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v = fmaxf(v, s[t][x][r]);
+        const float mx = quad_max(v);
+        const bool reset = !(quad_max(part[x]) <= kSumCap);
+        const float m_new = reset ? fmaxf(mx, m[x]) : m[x];
+        const float alpha = fast_exp2((m[x] - m_new) * a.scale_log2);
+        m[x] = m_new;
+        l[x] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt][x] *= alpha;
+        part[x] = expo(x);
       }
+    }
+    l[0] += part[0];
+    l[1] += part[1];
+
+    // O^T += V^T P^T, one 32-key step at a time.
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      bf16x8 vop[NDT];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        s16x4 xv[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int r = c * 32 + half * 16 + grp * 4 + src_row;
+          const int col = dt * 16 + src_col;
+          const __bf16* ptr = vt + r * D + (((col >> 3) ^ v_swz<D>(r)) << 3) + (col & 7);
+          xv[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)ptr);
+        }
+        vop[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(xv[0], xv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pb[0][c], o[dt][0], 0, 0, 0);
+        o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pb[1][c], o[dt][1], 0, 0, 0);
+      }
+    }
   };
 
   for (int j = j0; j < n_tiles; j += 2) {
@@ -393,7 +483,13 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, Bf16Cfg<D>::NW == 8 ? 1 : 2) void f
     if (j + 1 < n_tiles) tile(j + 1, ks1, vs1, ks0, vs0);
   }
 
-  fwd_epilogue<D>(a, b, h, tq, hh, st, o_t);
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    f32x4 ox[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) ox[dt] = o[dt][x];
+    fwd_epilogue16<D>(a, b, h, tq[x], grp, m[x], l[x], ox);
+  }
 }
 
 // ------------------------------------------------------------------------- fp32 path
