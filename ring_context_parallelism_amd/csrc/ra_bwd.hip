@@ -71,9 +71,8 @@ __device__ inline bf16x8 cat(s16x4 a, s16x4 b) {
 // LDS serves 16 lanes x 16 bytes per clock from 64 four-byte banks.
 //
 // Padded tile (read both ways): an odd row stride (3, 13 or 19 sixteen-byte chunks)
-// is conflict free for 16-byte reads of 16 rows that differ mod 16 at one column,
-// and, with the row order rho16 below, for transpose reads; it keeps every address
-// a per-lane base plus a compile-time offset.
+// keeps every address a per-lane base plus a compile-time offset and, with the row
+// order rho16 below, makes the transpose reads conflict free.
 template <int COLS>
 struct Pad {
   static constexpr int CH = COLS / 8;
@@ -84,7 +83,8 @@ struct Pad {
 
 // Swizzled tile (16-byte row reads only): XOR the chunk with the row's index among
 // the rows that share one 256-byte bank window, so 16 consecutive rows at one
-// logical chunk hit 16 distinct bank groups.
+// logical chunk hit 16 distinct bank groups and every quad of consecutive rows reads
+// one aligned 64-byte block (conflict free).
 template <int COLS>
 __device__ inline int xsw(int r) {
   constexpr int CH = COLS / 8, RPW = 256 / (COLS * 2);
@@ -93,6 +93,20 @@ __device__ inline int xsw(int r) {
 template <int COLS>
 __device__ inline int xoff(int r, int col) {  // element offset of column col (multiple of 8)
   return r * COLS + ((((col >> 3) ^ xsw<COLS>(r))) << 3);
+}
+
+// Tile row order of the 16x16x32 operands: logical row m = 16 h + 4 g + k (h: query
+// half, g: transpose-read lane group, k: row within the group) lives in tile row
+// 16 h + 2 (4 (g & 1) + k) + (g >> 1).  A transpose read (lane groups {0,1} or
+// {2,3}, 8 rows x 2 chunks) then touches 8 rows of one parity, which the odd padded
+// stride puts in 16 distinct bank groups: conflict free.  The 16-byte row reads of
+// such a tile take two passes: on this chip a 16-byte read is conflict free only if
+// every quad of consecutive lanes reads two aligned 32-byte blocks, and a quad's rows
+// lie inside one transpose block, which needs them in 4 distinct blocks (measured;
+// no row order satisfies both).
+__device__ inline int rho16(int m) {
+  const int g = (m >> 2) & 3;
+  return (m & 16) | ((((g & 1) << 2) | (m & 3)) << 1) | (g >> 1);
 }
 
 // Direct-to-LDS loads of rows r0..r0+ROWS-1 into a padded tile.  Pad slots, rows
@@ -115,8 +129,9 @@ __device__ inline void dma_pad(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, in
   }
 }
 
-// Direct-to-LDS loads of rows r0..r0+ROWS-1 into a swizzled tile.
-template <int ROWS, int COLS, int NT>
+// Direct-to-LDS loads of rows r0..r0+ROWS-1 into a swizzled tile.  With PERM, tile
+// row p holds global row r0 + rho16(p) (32-row tiles).
+template <int ROWS, int COLS, int NT, bool PERM = false>
 __device__ inline void dma_xor(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, int r0,
                                __bf16* tile, int wave, int lane) {
   constexpr int CH = COLS / 8;
@@ -128,7 +143,8 @@ __device__ inline void dma_xor(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, in
     if (SLOTS % NT != 0 && base >= SLOTS) break;  // wave-uniform
     const int slot = base + lane;
     const int r = slot / CH, pc = slot % CH;
-    const uint32_t off = (uint32_t)(r0 + r) * row_bytes + (uint32_t)((pc ^ xsw<COLS>(r)) * 16);
+    const int gr = PERM ? rho16(r) : r;
+    const uint32_t off = (uint32_t)(r0 + gr) * row_bytes + (uint32_t)((pc ^ xsw<COLS>(r)) * 16);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + base * 8), 16, off, 0, 0, 0);
   }
 }
@@ -139,16 +155,6 @@ constexpr int kKvThreads = 256;  // 4 waves, each 32 keys
 constexpr int kKvBN = 128;       // keys per workgroup
 constexpr int kKvBQ = 32;        // query rows per iteration
 
-// Tile row order of the 16x16x32 operands: logical row m = 16 h + 4 g + k (h: query
-// half, g: transpose-read lane group, k: row within the group) lives in tile row
-// 16 h + 2 (4 (g & 1) + k) + (g >> 1).  16-byte reads of the 16 rows of a half
-// touch 16 distinct rows, and a transpose read (lane groups {0,1} or {2,3}, 8 rows x
-// 2 chunks) touches 8 rows of one parity; with the odd padded stride both are
-// conflict free.
-__device__ inline int rho16(int m) {
-  const int g = (m >> 2) & 3;
-  return (m & 16) | ((((g & 1) << 2) | (m & 3)) << 1) | (g >> 1);
-}
 
 // PACKED: packed documents (a.seg != nullptr), a separate instantiation.
 //
@@ -579,9 +585,12 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int n = 0; n < NDT; ++n) dq_t[n][0] = dq_t[n][1] = f32x4{};
 
-  // Logical key l of a tile lives in tile row rho16(l) (K and V alike).  A-operand
-  // rows of S^T and dP^T: logical keys 16 t + l16; transpose-read sources of K^T:
-  // logical keys 16 hf + 4 grp + l16 / 4, columns 4 (l16 % 4) of a 16-column tile.
+  // Logical key l of a tile is global key j * kQBN + rho16(l).  The K tile, read
+  // both ways, keeps global row order, so key l sits in its row rho16(l); the V tile,
+  // read only by 16-byte row reads, is loaded permuted, so key l sits in its row l
+  // (with the XOR swizzle that keeps those reads conflict free).  A-operand rows of
+  // S^T and dP^T: logical keys 16 t + l16; transpose-read sources of K^T: logical keys
+  // 16 hf + 4 grp + l16 / 4, columns 4 (l16 % 4) of a 16-column tile.
   int krow[2], trow[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -593,7 +602,7 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 
   auto dma_kv = [&](int j, __bf16* kn, __bf16* vn) {
     dma_pad<kQBN, D, kQThreads>(kr_, kv_row, j * kQBN, kn, wave, lane);
-    dma_xor<kQBN, D, kQThreads>(vr_, kv_row, j * kQBN, vn, wave, lane);
+    dma_xor<kQBN, D, kQThreads, true>(vr_, kv_row, j * kQBN, vn, wave, lane);
   };
 
   auto tile = [&](int j, const __bf16* kt, const __bf16* vt, __bf16* kn, __bf16* vn) {
@@ -615,7 +624,7 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const bf16x8 ka = *(const bf16x8*)(kt + krow[t] * PS + kk * 32 + grp * 8);
-        const bf16x8 va = *(const bf16x8*)(vt + xoff<D>(krow[t], kk * 32 + grp * 8));
+        const bf16x8 va = *(const bf16x8*)(vt + xoff<D>(t * 16 + l16, kk * 32 + grp * 8));
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
           s[t][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qr[x][kk], s[t][x], 0, 0, 0);
