@@ -137,6 +137,7 @@ __device__ inline void dma_xor(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, in
   constexpr int CH = COLS / 8;
   constexpr int SLOTS = ROWS * CH;
   static_assert(SLOTS % 64 == 0, "tile must be whole wave loads");
+  static_assert(!PERM || ROWS == 32, "the row permutation is defined on 32-row tiles");
 #pragma unroll
   for (int it = 0; it < (SLOTS + NT - 1) / NT; ++it) {
     const int base = it * NT + wave * 64;
