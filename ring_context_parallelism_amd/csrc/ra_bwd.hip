@@ -229,22 +229,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
         q_hi[x] = 0;
       }
     }
-    if (tid == 0) {
-      red[0] = L;
-      red[1] = 0;
-      red[2] = 0;
-      red[3] = L;
-    }
-    __syncthreads();
-    atomicMin(&red[0], min(q_lo[0], q_lo[1]));
-    atomicMax(&red[1], max(q_hi[0], q_hi[1]));
-    atomicMax(&red[2], max(q_lo[0], q_lo[1]));
-    atomicMin(&red[3], min(q_hi[0], q_hi[1]));
-    __syncthreads();
-    t_first = red[0];
-    t_end = red[1];
-    full_lo = red[2];
-    full_hi = red[3];
+    wg_interval_reduce2(red, q_lo, q_hi, L, t_first, t_end, full_lo, full_hi);
   } else {  // dense: query t sees key u iff t >= count_le(cq, pos(ck, u) - 1)
     const int u_last = min(u0 + kKvBN, L) - 1;
     if (a.causal) {
@@ -556,22 +541,9 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
         kv_lim[x] = 0;
       }
     }
-    if (tid == 0) {
-      red[0] = L;
-      red[1] = 0;
-      red[2] = 0;
-      red[3] = L;
-    }
-    __syncthreads();
-    atomicMin(&red[0], min(kv_lo[0], kv_lo[1]));
-    atomicMax(&red[1], max(kv_lim[0], kv_lim[1]));
-    atomicMax(&red[2], max(kv_lo[0], kv_lo[1]));
-    atomicMin(&red[3], min(kv_lim[0], kv_lim[1]));
-    __syncthreads();
-    j0 = red[0] / kQBN;
-    n_keys = red[1];
-    full_lo = red[2];
-    n_full = red[3];
+    int min_lo;
+    wg_interval_reduce2(red, kv_lo, kv_lim, L, min_lo, n_keys, full_lo, n_full);
+    j0 = min_lo / kQBN;
   } else if (a.causal) {
     const int t_last = min(t0 + kQBM, L) - 1;
 #pragma unroll

@@ -342,22 +342,9 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, Bf16Cfg<D>::NW == 8 ? 1 : 2) void f
         kv_lim[x] = 0;
       }
     }
-    if (tid == 0) {
-      red[0] = L;
-      red[1] = 0;
-      red[2] = 0;
-      red[3] = L;
-    }
-    __syncthreads();
-    atomicMin(&red[0], min(kv_lo[0], kv_lo[1]));
-    atomicMax(&red[1], max(kv_lim[0], kv_lim[1]));
-    atomicMax(&red[2], max(kv_lo[0], kv_lo[1]));
-    atomicMin(&red[3], min(kv_lim[0], kv_lim[1]));
-    __syncthreads();
-    j0 = red[0] / BN;
-    n_keys = red[1];
-    full_lo = red[2];
-    n_full = red[3];
+    int min_lo;
+    wg_interval_reduce2(red, kv_lo, kv_lim, L, min_lo, n_keys, full_lo, n_full);
+    j0 = min_lo / BN;
   } else if (a.causal) {
     const int t_last = min(t0 + kBM, L) - 1;
 #pragma unroll

@@ -103,12 +103,14 @@ __host__ __device__ inline void query_interval(const LayoutMap& m, int32_t cq, i
 }
 
 #if defined(__HIPCC__)
-// Workgroup-wide (min lo, max hi, max lo, min hi) of per-lane intervals [lo, hi)
+// Workgroup-wide (min lo, max hi, max lo, min hi) of per-row intervals [lo, hi)
 // (packed documents): tiles from min lo to max hi hold every visible pair, and
-// [max lo, min hi) is visible to every lane.  red: 4 ints of LDS.  Every thread of
-// the workgroup must call it (two barriers).
-__device__ inline void wg_interval_reduce(int* red, int lo, int hi, int n, int& min_lo,
-                                          int& max_hi, int& max_lo, int& min_hi) {
+// [max lo, min hi) is visible to every row.  A lane holding several rows passes the
+// min and max of its rows' bounds.  red: 4 ints of LDS.  Every thread of the
+// workgroup must call it (two barriers).
+__device__ inline void wg_interval_reduce(int* red, int lo_min, int hi_max, int lo_max,
+                                          int hi_min, int n, int& min_lo, int& max_hi,
+                                          int& max_lo, int& min_hi) {
   if (threadIdx.x == 0) {
     red[0] = n;
     red[1] = 0;
@@ -116,15 +118,27 @@ __device__ inline void wg_interval_reduce(int* red, int lo, int hi, int n, int& 
     red[3] = n;
   }
   __syncthreads();
-  atomicMin(&red[0], lo);
-  atomicMax(&red[1], hi);
-  atomicMax(&red[2], lo);
-  atomicMin(&red[3], hi);
+  atomicMin(&red[0], lo_min);
+  atomicMax(&red[1], hi_max);
+  atomicMax(&red[2], lo_max);
+  atomicMin(&red[3], hi_min);
   __syncthreads();
   min_lo = red[0];
   max_hi = red[1];
   max_lo = red[2];
   min_hi = red[3];
+}
+// One row per lane.
+__device__ inline void wg_interval_reduce(int* red, int lo, int hi, int n, int& min_lo,
+                                          int& max_hi, int& max_lo, int& min_hi) {
+  wg_interval_reduce(red, lo, hi, lo, hi, n, min_lo, max_hi, max_lo, min_hi);
+}
+// Two rows per lane.
+__device__ inline void wg_interval_reduce2(int* red, const int (&lo)[2], const int (&hi)[2],
+                                           int n, int& min_lo, int& max_hi, int& max_lo,
+                                           int& min_hi) {
+  wg_interval_reduce(red, min(lo[0], lo[1]), max(hi[0], hi[1]), max(lo[0], lo[1]),
+                     min(hi[0], hi[1]), n, min_lo, max_hi, max_lo, min_hi);
 }
 #endif
 
