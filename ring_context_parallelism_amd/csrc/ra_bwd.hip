@@ -159,8 +159,8 @@ constexpr int kKvBQ = 32;        // query rows per iteration
 
 // PACKED: packed documents (a.seg != nullptr), a separate instantiation.
 //
-// 16x16x32 MFMA tiles (a stream of them sustains about 15% more FLOP/s than
-// 32x32x16 tiles under the board power limit, and this kernel runs at that limit).
+// 16x16x32 MFMA tiles: a stream of them sustains about 15% more FLOP/s than 32x32x16
+// tiles under the board power limit, which held this kernel back on 32x32x16 tiles.
 // Accumulator layout of a 16x16 tile: lane l holds column l % 16 and rows
 // 4 (l / 16) + r; operands hold row (A) or column (B) l % 16 and contraction
 // indices 8 (l / 16) + j.  S and dP are computed as [query][key] tiles, so each lane

@@ -47,9 +47,9 @@ struct Bf16Cfg {
   static constexpr int BM = 32 * NW;  // query rows
 };
 
-// The two halves of a wave (lanes l and l ^ 32) hold the same query rows.
-// permlane32_swap returns (own, partner) in lanes < 32 and (partner, own) in lanes
-// >= 32, so a max or a sum of the pair needs no select.
+// Max and sum over lanes l and l ^ 32 (the two halves of a wave).  permlane32_swap
+// returns (own, partner) in lanes < 32 and (partner, own) in lanes >= 32, so a max or
+// a sum of the pair needs no select.
 __device__ inline float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -71,12 +71,14 @@ __device__ inline int xcd_remap(int bid, int nblk) {
   return rem * per + (xcd - rem) * (per - 1) + slot;
 }
 
+// Row state of the fp32 kernel, whose 32x32 accumulators give every lane one query
+// row and the two halves of a wave the same rows.
 struct RowState {
   float m;  // running max of raw scores (shared by the two halves of a row)
   float l;  // running sum of exp2((s - m) * scale_log2) over this lane's keys
 };
 
-// Epilogue shared by both dtypes: normalise, optionally LSE-merge, store.
+// Epilogue of the fp32 kernel: normalise, optionally LSE-merge, store.
 // o_t[n] holds O^T[d][q] for d = dblk*32 + (i/4)*8 + hh*4 + i%4 with n = dblk*16 + i.
 template <int D>
 __device__ inline void fwd_epilogue(const FwdArgs& a, int b, int h, int tq, int hh,
