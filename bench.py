@@ -506,11 +506,7 @@ def main():
         ev[1].record(stream)
         if not w.backward:
             return
-        ra.ra_bwd_delta(prob, out, share.do, delta, stream=stream)
-        dq.zero_()
-        for c in range(w.world):
-            dks[c].zero_()
-            dvs[c].zero_()
+        ra.ra_bwd_prepare(prob, out, share.do, delta, dq, dks, dvs, stream=stream)
         ev[2].record(stream)
         for i, st in enumerate(steps):
             c = st["chunk"]

@@ -192,13 +192,28 @@ ra_status_t ra_block_attn_bwd_dq(const ra_problem_t* prob, const void* q, int32_
                                  const float* lse, const float* delta, float* dq,
                                  hipStream_t stream);
 
+/*
+ * Backward prologue of one rank (ringmaster page, "Status": flash-style,
+ * reverse-ring backward): delta as in ra_bwd_delta, then zero-fills dq (fp32
+ * [B, Hq, L, D]) and, for every chunk c < p, dk_chunks[c] and dv_chunks[c] (fp32
+ * [B, Hkv, L, D]; HOST arrays of p device pointers), so the step kernels can
+ * accumulate into them.  The fills are kernels of this library, not memset nodes,
+ * so a caller may capture the call into a graph.  Every pointer must be 16-byte
+ * aligned.  Errors: the problem checks of the other entry points, RA_ERR_NULL for
+ * a NULL pointer and RA_ERR_SHAPE for a misaligned one, all before anything is
+ * launched; RA_ERR_HIP for a failed launch.
+ */
+ra_status_t ra_bwd_prepare(const ra_problem_t* prob, const void* out, const void* dout,
+                           float* delta, float* dq, float* const* dk_chunks,
+                           float* const* dv_chunks, hipStream_t stream);
+
 /* Bytes of device workspace ra_ring_bwd needs (fp32 delta [B, Hq, L]). */
 ra_status_t ra_ring_bwd_workspace_size(const ra_problem_t* prob, size_t* bytes);
 
 /*
- * The ring driver, backward, for rank `rank`: computes delta into ws, zero-fills
- * dq and every dk_chunks[c], dv_chunks[c], then accumulates every step with a
- * visible pair.  out / lse are the forward's results for this rank.  dk_chunks and
+ * The ring driver, backward, for rank `rank`: runs ra_bwd_prepare (delta into
+ * ws; dq and every dk_chunks[c], dv_chunks[c] zero-filled), then accumulates every
+ * step with a visible pair.  out / lse are the forward's results for this rank.  dk_chunks and
  * dv_chunks are HOST arrays of p device pointers (fp32 [B, Hkv, L, D]); the result
  * is this rank's share of the gradients (its queries only).
  */

@@ -360,6 +360,30 @@ ra_status_t ra_bwd_delta(const ra_problem_t* prob, const void* out, const void* 
   return ok();
 }
 
+ra_status_t ra_bwd_prepare(const ra_problem_t* prob, const void* out, const void* dout,
+                           float* delta, float* dq, float* const* dk_chunks,
+                           float* const* dv_chunks, hipStream_t stream) {
+  RA_TRY(check_problem(prob));
+  RA_TRY(check_ptr(dq, "dq"));
+  if (dk_chunks == nullptr || dv_chunks == nullptr) return fail(RA_ERR_NULL, "chunk array is NULL");
+  for (int c = 0; c < prob->world; ++c) {
+    RA_TRY(check_ptr(dk_chunks[c], "dk_chunks[c]"));
+    RA_TRY(check_ptr(dv_chunks[c], "dv_chunks[c]"));
+  }
+  RA_TRY(ra_bwd_delta(prob, out, dout, delta, stream));
+  const int64_t L = prob->seq_total / prob->world;
+  const int64_t D = prob->head_dim_padded;
+  hipError_t e = ra::launch_fill_f32(dq, prob->batch * prob->heads_q * L * D, 0.0f, stream);
+  if (e != hipSuccess) return hip_fail(e, "ra_bwd_prepare fill");
+  const int64_t nkv = prob->batch * prob->heads_kv * L * D;
+  for (int c = 0; c < prob->world; ++c) {
+    e = ra::launch_fill_f32(dk_chunks[c], nkv, 0.0f, stream);
+    if (e == hipSuccess) e = ra::launch_fill_f32(dv_chunks[c], nkv, 0.0f, stream);
+    if (e != hipSuccess) return hip_fail(e, "ra_bwd_prepare fill");
+  }
+  return ok();
+}
+
 static ra_status_t bwd_supported(const ra_problem_t* prob) {
   if (prob->dtype != RA_BF16)
     return fail(RA_ERR_UNSUPPORTED, "the backward supports bf16 only");
@@ -491,26 +515,14 @@ ra_status_t ra_ring_bwd(const ra_problem_t* prob, int32_t rank, const void* q,
   if (((uintptr_t)ws & 255u) != 0) return fail(RA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   const ra::LayoutMap m = make_map(prob);
   float* delta = (float*)ws;
-  const int32_t L = m.L;
   const int64_t D = prob->head_dim_padded;
-  hipError_t e = ra::launch_bwd_delta(prob->dtype, (int32_t)prob->batch, (int32_t)prob->heads_q, L,
-                                      (int32_t)D, out, dout, prob->o_stride[0], prob->o_stride[1],
-                                      prob->o_stride[2], delta, stream);
-  if (e != hipSuccess) return hip_fail(e, "ra_ring_bwd delta launch");
-  e = ra::launch_fill_f32(dq, prob->batch * prob->heads_q * L * D, 0.0f, stream);
-  if (e != hipSuccess) return hip_fail(e, "ra_ring_bwd fill");
-  const int64_t nkv = prob->batch * prob->heads_kv * L * D;
-  for (int c = 0; c < prob->world; ++c) {
-    e = ra::launch_fill_f32(dk_chunks[c], nkv, 0.0f, stream);
-    if (e == hipSuccess) e = ra::launch_fill_f32(dv_chunks[c], nkv, 0.0f, stream);
-    if (e != hipSuccess) return hip_fail(e, "ra_ring_bwd fill");
-  }
+  RA_TRY(ra_bwd_prepare(prob, out, dout, delta, dq, dk_chunks, dv_chunks, stream));
   for (int s = 0; s < prob->world; ++s) {
     const int c = ((rank - s) % prob->world + prob->world) % prob->world;
     if (!step_live(prob, m, rank, c)) continue;
     ra::BwdArgs a = bwd_args(prob, q, rank, k_chunks[c], v_chunks[c], c, dout, lse, delta, dq,
                              dk_chunks[c], dv_chunks[c]);
-    e = ra::launch_bwd(prob->dtype, (int)D, a, 3, stream);
+    const hipError_t e = ra::launch_bwd(prob->dtype, (int)D, a, 3, stream);
     if (e != hipSuccess) return hip_fail(e, "ra_ring_bwd launch");
   }
   return ok();

@@ -28,7 +28,7 @@ DTYPE_IDS = {"f32": RA_F32, "bf16": RA_BF16}
 
 EXPORTS = [
     "ra_block_attn_fwd", "ra_lse_merge", "ra_ring_workspace_size", "ra_ring_fwd",
-    "ra_bwd_delta", "ra_block_attn_bwd", "ra_block_attn_bwd_dkdv", "ra_block_attn_bwd_dq",
+    "ra_bwd_delta", "ra_bwd_prepare", "ra_block_attn_bwd", "ra_block_attn_bwd_dkdv", "ra_block_attn_bwd_dq",
     "ra_ring_bwd_workspace_size", "ra_ring_bwd",
     "ra_positions", "ra_visible_pairs", "ra_visible_pairs_packed", "ra_status_str",
     "ra_last_error",
@@ -74,6 +74,7 @@ def lib():
             "ra_ring_workspace_size": [_PROB, ctypes.POINTER(_SZ)],
             "ra_ring_fwd": [_PROB, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
             "ra_bwd_delta": [_PROB, _P, _P, _P, _P],
+            "ra_bwd_prepare": [_PROB, _P, _P, _P, _P, _P, _P, _P],
             "ra_block_attn_bwd": [_PROB, _P, _I32, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P],
             "ra_block_attn_bwd_dkdv": [_PROB, _P, _I32, _P, _P, _I32, _P, _P, _P, _P, _P, _P],
             "ra_block_attn_bwd_dq": [_PROB, _P, _I32, _P, _P, _I32, _P, _P, _P, _P, _P],
@@ -185,6 +186,11 @@ def ra_ring_fwd(prob, rank, q, k_chunks, v_chunks, out, lse, ws, ws_bytes=None, 
 def ra_bwd_delta(prob, out, dout, delta, stream=None):
     _check(lib().ra_bwd_delta(ctypes.byref(prob), _ptr(out), _ptr(dout), _ptr(delta),
                               _stream(stream)))
+
+
+def ra_bwd_prepare(prob, out, dout, delta, dq, dk_chunks, dv_chunks, stream=None):
+    _check(lib().ra_bwd_prepare(ctypes.byref(prob), _ptr(out), _ptr(dout), _ptr(delta), _ptr(dq),
+                                _ptr_array(dk_chunks), _ptr_array(dv_chunks), _stream(stream)))
 
 
 def ra_block_attn_bwd(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dq, dk, dv,

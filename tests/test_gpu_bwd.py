@@ -113,6 +113,35 @@ def test_bwd_delta_kernel():
         assert np.max(np.abs(delta.cpu().numpy() - want)) < 1e-4
 
 
+def test_bwd_prepare_delta_and_zero_fill():
+    """ra_bwd_prepare: delta as the oracle's, every gradient buffer exactly zero.
+
+    The buffers start as NaN and each has a NaN guard tail (odd L, p = 3 chunks,
+    GQA), so a fill that stops short, overruns or misses a chunk shows.
+    """
+    dev = need_gpu()
+    B, H, Hkv, p, L, D = 2, 4, 2, 3, 79, 64
+    rng = np.random.default_rng(11)
+    o = torch.tensor(rng.standard_normal((B, H, L, D)), dtype=torch.bfloat16)
+    do = torch.tensor(rng.standard_normal((B, H, L, D)), dtype=torch.bfloat16)
+    prob = ra.make_problem(batch=B, heads_q=H, heads_kv=Hkv, head_dim=D, head_dim_padded=D,
+                           seq_total=p * L, world=p, layout="contiguous", causal=True,
+                           dtype="bf16")
+    nan = dict(dtype=torch.float32, device=dev)
+    guard = 4096  # a tail past every buffer, which must stay NaN
+    delta = torch.full((B * H * L,), float("nan"), **nan)
+    dq = torch.full((B * H * L * D + guard,), float("nan"), **nan)
+    dks = [torch.full((B * Hkv * L * D + guard,), float("nan"), **nan) for _ in range(p)]
+    dvs = [torch.full((B * Hkv * L * D + guard,), float("nan"), **nan) for _ in range(p)]
+    ra.ra_bwd_prepare(prob, o.to(dev), do.to(dev), delta, dq, dks, dvs)
+    torch.cuda.synchronize()
+    want = oracle.bwd_delta(do.float().numpy(), o.float().numpy()).reshape(-1)
+    assert np.max(np.abs(delta.cpu().numpy() - want)) < 1e-4
+    for t, n in [(dq, B * H * L * D)] + [(x, B * Hkv * L * D) for x in dks + dvs]:
+        assert torch.count_nonzero(t[:n]).item() == 0
+        assert torch.isnan(t[n:]).all()
+
+
 def test_full_size_backward_sampled_and_identities():
     dev = need_gpu()
     w = WORKLOADS["zigzag_fwdbwd"]
