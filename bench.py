@@ -444,6 +444,28 @@ def aux_bench(reps=50):
     print(json.dumps(out), flush=True)
 
 
+def time_fwd_steps(ra, prob, w, share, steps, ws, stream, reps):
+    """Milliseconds of each live forward step launched on its own, one array per step.
+
+    The steps run in ring order through ra_block_attn_fwd: the first writes the fp32
+    workspace, the others merge into it, as in the ring driver (whose last launch
+    writes the output dtype instead).  One untimed pass comes first."""
+    import numpy as np
+    import torch
+    lse = torch.empty((w.batch, w.heads_q, w.chunk_len), dtype=torch.float32, device=ws.device)
+    n = len(steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(reps + 1)]
+    for e in ev:
+        e[0].record(stream)
+        for i, st in enumerate(steps):
+            c = st["chunk"]
+            ra.ra_block_attn_fwd(prob, share.q, w.rank, share.k_chunks[c], share.v_chunks[c], c,
+                                 ws, lse, ra.RA_WRITE if i == 0 else ra.RA_MERGE, stream=stream)
+            e[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [np.array([e[i].elapsed_time(e[i + 1]) for e in ev[1:]]) for i in range(n)]
+
+
 def main():
     args = parse()
     if args.aux:
@@ -540,17 +562,24 @@ def main():
     value = (fwd_flop + bwd_flop) / (ms_per_step * 1e-3) / 1e12
 
     fwd_step_ms = float(np.mean(fwd_ms)) / len(steps)  # the driver launches one kernel per live step
+    # Per-step forward times: the driver is timed as a whole above, so each live step
+    # is launched once more on its own (ra_block_attn_fwd, WRITE then MERGE into the
+    # fp32 workspace), with events around every launch, after the timed region.
+    step_fwd = time_fwd_steps(ra, prob, w, share, steps, ws, stream, max(3, args.steps))
     detail = []
     for i, st in enumerate(steps):
+        sm = step_fwd[i]
         d = dict(step=st["step"], chunk=st["chunk"],
                  visible_pairs_per_head=st["visible_pairs_per_head"],
-                 fwd_ms_est=fwd_step_ms,
-                 fwd_tflops=st["fwd_flop"] / (fwd_step_ms * 1e-3) / 1e12)
+                 fwd_ms=float(np.mean(sm)), fwd_ms_median=float(np.median(sm)),
+                 fwd_ms_min=float(np.min(sm)),
+                 fwd_tflops=st["fwd_flop"] / (float(np.mean(sm)) * 1e-3) / 1e12)
         if w.backward:
             kv_ms = np.array([e[2 + 2 * i].elapsed_time(e[3 + 2 * i]) for e in events])
             q_ms = np.array([e[3 + 2 * i].elapsed_time(e[4 + 2 * i]) for e in events])
             bms = kv_ms + q_ms
-            d.update(bwd_ms=float(np.mean(bms)), bwd_ms_min=float(np.min(bms)),
+            d.update(bwd_ms=float(np.mean(bms)), bwd_ms_median=float(np.median(bms)),
+                     bwd_ms_min=float(np.min(bms)),
                      bwd_dkdv_ms=float(np.mean(kv_ms)), bwd_dq_ms=float(np.mean(q_ms)),
                      bwd_tflops=st["bwd_flop"] / (float(np.mean(bms)) * 1e-3) / 1e12)
         d["fwd_pct_peak"] = 100.0 * d["fwd_tflops"] / peak
