@@ -351,24 +351,32 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
         dp[hf][x] = nd;
       }
     }
+    // All S MFMAs first, then dP: the exponentials of S need only the former, and
+    // the shorter live ranges of the operands keep the kernel free of spills.
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      bf16x8 vbv[2], qa[2], da[2];
+      bf16x8 qa[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) qa[hf] = *(const bf16x8*)(qt + arow[hf] + kk * 32);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+          s[hf][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hf], kreg[x][kk], s[hf][x], 0, 0, 0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      bf16x8 vbv[2], da[2];
 #pragma unroll
       for (int x = 0; x < 2; ++x)
         vbv[x] = *(const bf16x8*)(s_v + xoff<D>(krow[x], kk * 32 + grp * 8));
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        qa[hf] = *(const bf16x8*)(qt + arow[hf] + kk * 32);
-        da[hf] = *(const bf16x8*)(dot + arow[hf] + kk * 32);
-      }
+      for (int hf = 0; hf < 2; ++hf) da[hf] = *(const bf16x8*)(dot + arow[hf] + kk * 32);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          s[hf][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hf], kreg[x][kk], s[hf][x], 0, 0, 0);
+        for (int x = 0; x < 2; ++x)
           dp[hf][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[hf], vbv[x], dp[hf][x], 0, 0, 0);
-        }
     }
 
     // P = exp2(S*scale_log2 - LSE*log2 e), dS = P (dP - delta).  Accumulator row r
