@@ -224,7 +224,9 @@ def trace_summary(run_dir, workload):
              f"{len(steps)} live ring steps per bench step; {pairs:.4g} visible (query, key) pairs "
              "per launch summed over batch and heads.  Algorithmic FLOP per launch: forward 4d, "
              "dK/dV kernel 8d (S, dP, dV, dK), dQ kernel 2d (its recomputation of S and dP is "
-             "not counted) per pair.", "",
+             "not counted) per pair.  The forward kernel's calls include the per-step "
+             "timing pass that follows the timed steps (each live step launched once more "
+             "on its own).", "",
              "| kernel | calls | average (ms) | min (ms) | max (ms) | share | algorithmic "
              "TFLOP/s | of peak |", "|---|---|---|---|---|---|---|---|"]
     for r in rows:
