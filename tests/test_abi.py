@@ -166,6 +166,15 @@ def test_call_validation():
                       FAKE, 0) == ra.RA_ERR_UNSUPPORTED
     assert _status_of(ra.ra_ring_bwd, p, 0, FAKE, ks, ks, FAKE, FAKE, FAKE, FAKE, ks, ks,
                       FAKE, 8, 0) == ra.RA_ERR_WORKSPACE
+    # ra_bwd_prepare checks every pointer before its first launch
+    prep = ra.ra_bwd_prepare
+    assert _status_of(prep, p, FAKE, FAKE, FAKE, 0, ks, ks, 0) == ra.RA_ERR_NULL
+    assert _status_of(prep, p, FAKE, FAKE, FAKE, FAKE, ks[:3] + [0], ks, 0) == ra.RA_ERR_NULL
+    assert _status_of(prep, p, FAKE, FAKE, FAKE, FAKE, ks, [FAKE + 2] + ks[1:], 0) == \
+        ra.RA_ERR_SHAPE
+    assert _status_of(prep, p, 0, FAKE, FAKE, FAKE, ks, ks, 0) == ra.RA_ERR_NULL
+    assert _status_of(prep, p, FAKE, FAKE, 0, FAKE, ks, ks, 0) == ra.RA_ERR_NULL
+    assert _status_of(prep, _prob(world=0), FAKE, FAKE, FAKE, FAKE, ks, ks, 0) == ra.RA_ERR_SHAPE
 
 
 def test_status_strings():
