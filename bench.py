@@ -163,8 +163,9 @@ def sq_summary(root, workload, n_cu=256):
     lines += [cmd.format(c=c, i=i + 1, w=workload) for i, c in enumerate(SQ_PASSES)]
     lines += ["python3 <repo>/bench.py --sq-summary <out>", "```", "",
               "Cycle counters are summed over the chip (`SQ_BUSY_CU_CYCLES` over 256 CUs, "
-              "`SQ_VALU_MFMA_BUSY_CYCLES` over 1024 SIMDs; the latter equals 32 x the MFMA "
-              "count, one 32x32x16 MFMA taking 32 clocks).  Effective clock = "
+              "`SQ_VALU_MFMA_BUSY_CYCLES` over 1024 SIMDs; the latter counts the clocks each "
+              "MFMA occupies: 16 for a 16x16x32 bf16 tile, 32 for a 32x32x16 one).  Effective "
+              "clock = "
               "`SQ_BUSY_CU_CYCLES` / 256 / kernel duration.  VALU instructions per SIMD-cycle = "
               "`SQ_INSTS_VALU` / (4 `SQ_BUSY_CU_CYCLES`); waves per SIMD = `SQ_WAVE_CYCLES` / "
               "`SQ_BUSY_CU_CYCLES` (`SQ_WAVE_CYCLES` counts in units of 4 cycles).", "",
