@@ -17,7 +17,10 @@
  *  * Tensors in the problem dtype (q, every k and v chunk, out, dout) are
  *    [B, H, L, D] with element strides (b, h, t) given in the problem and a unit
  *    stride along D; every row must start 16-byte aligned.  Columns
- *    head_dim..D-1 of q, k and v must be zero (storage padding).
+ *    head_dim..D-1 of q, k and v must be zero (storage padding).  Within one
+ *    (b, h), (L + 256) rows at the t stride must span less than 4 GiB for q, the
+ *    k/v chunks and out/dout (kernels address a head's rows with 32-bit offsets):
+ *    RA_ERR_UNSUPPORTED otherwise.
  *  * fp32 buffers (partial/accumulated outputs o, dq, dk, dv) are contiguous
  *    [B, H, L, D]; lse and delta are contiguous [B, Hq, L].  LSE is the natural
  *    log of sum_j exp(scaled score); a row that sees no key has o = 0 and

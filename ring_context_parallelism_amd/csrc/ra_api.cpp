@@ -80,8 +80,9 @@ ra_status_t check_problem(const ra_problem_t* p) {
     }
   const int64_t L = p->seq_total / p->world;
   // The kernels address rows inside one head with 32-bit buffer offsets (a tile may
-  // run up to 256 rows past the chunk end, where loads return zeros).
-  for (int i = 0; i < 2; ++i)
+  // run up to 256 rows past the chunk end, where loads return zeros); the backward
+  // reads dout that way too.
+  for (int i = 0; i < 3; ++i)
     if ((L + 256) * strides[i][2] * es >= (int64_t(1) << 32))
       return fail(RA_ERR_UNSUPPORTED, "%s[2] too large: one head's rows must span < 4 GiB",
                   names[i]);

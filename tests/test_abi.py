@@ -131,6 +131,8 @@ FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced on thes
     (dict(layout=7), ra.RA_ERR_UNSUPPORTED),
     (dict(dtype=9), ra.RA_ERR_UNSUPPORTED),
     (dict(q_stride=(0, 0, 3)), ra.RA_ERR_SHAPE),
+    (dict(kv_stride=(0, 0, 1 << 24)), ra.RA_ERR_UNSUPPORTED),  # a head's rows span > 4 GiB
+    (dict(o_stride=(0, 0, 1 << 24)), ra.RA_ERR_UNSUPPORTED),
     (dict(scale=-1.0), ra.RA_ERR_SHAPE),
     (dict(seg_bounds=FAKE, seg_count=1), ra.RA_ERR_SHAPE),
     (dict(seg_bounds=FAKE, seg_count=0), ra.RA_ERR_SHAPE),
