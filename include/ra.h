@@ -134,7 +134,8 @@ ra_status_t ra_block_attn_fwd(const ra_problem_t* prob, const void* q, int32_t q
  *   lse := log(exp(lse_acc) + exp(lse_part))
  *   o   := o_acc * exp(lse_acc - lse) + o_part * exp(lse_part - lse)
  * A part with lse = -inf is the identity (the accumulator is left unchanged when
- * lse_part = -inf).  d in 1..1024, d % 4 == 0; pointers 16-byte aligned.
+ * lse_part = -inf).  d in 4..1024, d % 4 == 0; rows in [0, 2^34); pointers
+ * 16-byte aligned.
  */
 ra_status_t ra_lse_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc,
                          const float* o_part, const float* lse_part, hipStream_t stream);

@@ -280,7 +280,8 @@ ra_status_t ra_block_attn_fwd(const ra_problem_t* prob, const void* q, int32_t q
 
 ra_status_t ra_lse_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc,
                          const float* o_part, const float* lse_part, hipStream_t stream) {
-  if (rows < 0) return fail(RA_ERR_SHAPE, "rows must be >= 0");
+  if (rows < 0 || rows >= (int64_t(1) << 34))
+    return fail(RA_ERR_SHAPE, "rows must be in [0, 2^34) (one launch)");
   if (d < 4 || d > 1024 || d % 4 != 0) return fail(RA_ERR_SHAPE, "d must be in [4, 1024], d %% 4 == 0");
   if (rows == 0) return ok();
   RA_TRY(check_ptr(o_acc, "o_acc"));

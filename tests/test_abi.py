@@ -161,6 +161,9 @@ def test_call_validation():
     assert _status_of(ring, p, 4, FAKE, ks, ks, FAKE, FAKE, FAKE, 1 << 30, 0) == ra.RA_ERR_SHAPE
     assert _status_of(ring, p, 1, FAKE, ks[:3] + [0], ks, FAKE, FAKE, FAKE, 1 << 30, 0) == ra.RA_ERR_NULL
     assert _status_of(ra.ra_lse_merge, 10, 6, FAKE, FAKE, FAKE, FAKE, 0) == ra.RA_ERR_SHAPE
+    assert _status_of(ra.ra_lse_merge, 10, 2048, FAKE, FAKE, FAKE, FAKE, 0) == ra.RA_ERR_SHAPE
+    assert _status_of(ra.ra_lse_merge, -1, 8, FAKE, FAKE, FAKE, FAKE, 0) == ra.RA_ERR_SHAPE
+    assert _status_of(ra.ra_lse_merge, 1 << 34, 8, FAKE, FAKE, FAKE, FAKE, 0) == ra.RA_ERR_SHAPE
     assert _status_of(ra.ra_lse_merge, 10, 8, 0, FAKE, FAKE, FAKE, 0) == ra.RA_ERR_NULL
     f32 = _prob(dtype="f32")
     bwd = ra.ra_block_attn_bwd
