@@ -34,6 +34,8 @@ CSRC = os.path.join(ROOT, "ring_context_parallelism_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_BYTES = 1 << 30
 # kernel key -> (substring of the device function's name, sources it is built from)
+WARM_SECONDS = 0.5  # default untimed warmup work, seconds
+
 KERNELS = {
     "fwd_kernel": ("fwd_bf16_kernel", ("ra_fwd.hip", "ra_internal.h")),
     "fwd_kernel_f32": ("fwd_f32_kernel", ("ra_fwd.hip", "ra_internal.h")),
@@ -46,7 +48,10 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default: at least 2, and enough for about "
+                         f"{WARM_SECONDS} s of work, so that short workloads run at the "
+                         "clock a sustained load settles at)")
     ap.add_argument("--workload", default="zigzag_fwdbwd")
     ap.add_argument("--dtype", default=None, help="override the workload dtype (f32|bf16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -544,9 +549,23 @@ def main():
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
               for _ in range(args.steps)]
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     warm = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    for _ in range(args.warmup):
+    if args.warmup is None:
+        # Default: at least 2 steps and about WARM_SECONDS of work.  The chip's clock
+        # settles only under sustained load, which a few steps of a short workload
+        # do not give.
+        one_step(warm)  # the first step also loads the kernels: not timed
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        one_step(warm)
+        torch.cuda.synchronize()
+        per = max(time.perf_counter() - t0, 1e-6)
+        todo = min(5000, int(WARM_SECONDS / per))
+        args.warmup = 2 + todo
+    else:
+        todo = args.warmup
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(todo):
         one_step(warm)
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
