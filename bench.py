@@ -492,8 +492,8 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU ring exchange is a design note, not part of this path).",
+        print(f"bench.py: this path runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU ring exchange is designed but not implemented).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -25,7 +25,7 @@ What it computes is the plain definition that the blockwise method reaches exact
   rank's rows (the "flash-style reverse-ring backward" of the ringmaster page,
   "Status", recomputes exactly these quantities).
 
-Readings taken where the pages are silent (each is listed in the design doc as well):
+Readings taken where the pages are silent:
 
 * scale = 1/sqrt(d_true): the sqrt(d) of the formula is the model's head dim;
   storage padding of the head dim is not the oracle's concern;
