@@ -83,6 +83,36 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
+def _logged_hashes(*logs):
+    """Kernel source hashes printed by the bench runs that took a set of counters (one
+    dict), or None when a log is missing or the runs disagree."""
+    seen = None
+    for log in logs:
+        if not os.path.exists(log):
+            return None
+        found = None
+        for line in open(log):
+            if line.startswith("[bench] source hashes "):
+                found = json.loads(line[len("[bench] source hashes "):])
+        if found is None or (seen is not None and found != seen):
+            return None
+        seen = found
+    return seen
+
+
+def _check_workload(log, workload):
+    """Refuses to summarise a run of another workload than the one named (the bench line
+    in the run's log names the workload it ran)."""
+    if not os.path.exists(log):
+        return
+    for line in open(log):
+        if line.startswith("{") and '"config"' in line:
+            ran = json.loads(line)["config"]["workload"]
+            if ran != workload:
+                raise SystemExit(f"bench.py: {log} is a run of {ran}, not {workload} "
+                                 f"(pass --workload {ran})")
+
+
 def _counter_kib(run_dir, counter):
     """Mean counter value (KiB) per dispatch, keyed by kernel name, from a --pmc run."""
     acc = {}
@@ -96,6 +126,7 @@ def _counter_kib(run_dir, counter):
 def pmc_summary(root, workload):
     """Traffic per dispatch from FETCH_SIZE and WRITE_SIZE, each scaled by what the same
     counter reads for a plain device copy of COPY_PROBE_BYTES."""
+    _check_workload(os.path.join(root, "pmc_fetch.log"), workload)
     fetch = _counter_kib(os.path.join(root, "pmc_fetch"), "FETCH_SIZE")
     write = _counter_kib(os.path.join(root, "pmc_write"), "WRITE_SIZE")
     cf = _counter_kib(os.path.join(root, "pmc_copy_fetch"), "FETCH_SIZE")
@@ -120,6 +151,7 @@ def pmc_summary(root, workload):
               f"so bytes = FETCH_SIZE x 1024 x {f_factor:.3f} and WRITE_SIZE x 1024 x {w_factor:.3f}.",
               "", "| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | fetched (GB) | "
               "written (GB) | traffic (GB) |", "|---|---|---|---|---|---|---|"]
+    logged = _logged_hashes(os.path.join(root, "pmc_fetch.log"), os.path.join(root, "pmc_write.log")) or {}
     data = {"workload": workload, "fetch_factor": f_factor, "write_factor": w_factor, "kernels": {}}
     for key, (sub, files) in KERNELS.items():
         name = next((k for k in fetch if sub in k), None)
@@ -127,14 +159,15 @@ def pmc_summary(root, workload):
             continue
         fb = fetch[name][0] * 1024.0 * f_factor
         wb = write[name][0] * 1024.0 * w_factor
-        data["kernels"][key] = {"name": name, "source_hash": source_hash(files),
+        data["kernels"][key] = {"name": name, "source_hash": logged.get(key),
                                 "fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb}
         lines.append(f"| `{name[:80]}` | {fetch[name][1]} | {fetch[name][0]:.0f} | "
                      f"{write[name][0]:.0f} | {fb / 1e9:.3f} | {wb / 1e9:.3f} | "
                      f"{(fb + wb) / 1e9:.3f} |")
-    lines += ["", "Source hashes (sha256 prefix of the kernel's source files) identify the kernel "
-              "build the counters were taken on; `bench.py` reports `traffic` only while they "
-              "match.", "", "```json", json.dumps(data, indent=1), "```", ""]
+    lines += ["", "Source hashes (sha256 prefix of the kernel's source files, as printed by the "
+              "profiled bench runs) identify the kernel build the counters were taken on; "
+              "`bench.py` reports `traffic` only while they match.", "", "```json",
+              json.dumps(data, indent=1), "```", ""]
     return "\n".join(lines)
 
 
@@ -150,6 +183,7 @@ SQ_PASSES = (
 
 def sq_summary(root, workload, n_cu=256):
     """Per-kernel ratios from three SQ-counter passes (one launch of each kernel per step)."""
+    _check_workload(os.path.join(root, "cnt_1.log"), workload)
     agg, dur = {}, {}
     for i in range(len(SQ_PASSES)):
         with open(os.path.join(root, f"cnt_{i + 1}", "run_counter_collection.csv")) as fh:
@@ -178,10 +212,18 @@ def sq_summary(root, workload, n_cu=256):
               "| LDS bank-conflict share | VALU / MFMA | LDS / MFMA | SALU / MFMA | wait-any / wave cycles "
               "| VALU instr per SIMD-cycle | waves per SIMD |",
               "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    logged = _logged_hashes(*[os.path.join(root, f"cnt_{i + 1}.log")
+                              for i in range(len(SQ_PASSES))]) or {}
+    data = {"workload": workload, "kernels": {}}
     for key, c in agg.items():
         m = {k: sum(v) / len(v) for k, v in c.items()}
         t = sum(dur[key].values()) / len(dur[key])
         busy = m["SQ_BUSY_CU_CYCLES"]
+        data["kernels"][key] = {
+            "name": KERNELS[key][0], "source_hash": logged.get(key),
+            "mfma_busy": round(m["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * busy), 4),
+            "effective_clock_ghz": round(busy / n_cu / t / 1e9, 3),
+            "lds_busy": round(m["SQ_LDS_IDX_ACTIVE"] / busy, 4)}
         lines.append(
             f"| `{KERNELS[key][0]}` | {t * 1e3:.2f} | {busy / n_cu / t / 1e9:.2f} | "
             f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * busy):.3f} | "
@@ -192,7 +234,9 @@ def sq_summary(root, workload, n_cu=256):
             f"{m['SQ_INSTS_SALU'] / m['SQ_INSTS_MFMA']:.2f} | "
             f"{m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.3f} | "
             f"{m['SQ_INSTS_VALU'] / (4 * busy):.3f} | {m['SQ_WAVE_CYCLES'] / busy:.2f} |")
-    lines.append("")
+    lines += ["", "Read by `bench.py`, which attaches a kernel's figures to its `roofline` only "
+              "while the `source_hash` printed by the profiled runs matches the current "
+              "sources:", "", "```json", json.dumps(data, indent=1), "```", ""]
     return "\n".join(lines)
 
 
@@ -215,6 +259,7 @@ def trace_summary(run_dir, workload):
     rows = list(csv.DictReader(open(os.path.join(run_dir, "run_kernel_stats.csv"))))
     bench_line = None
     log = run_dir.rstrip("/") + ".log"
+    _check_workload(log, workload)
     if os.path.exists(log):
         for line in open(log):
             if line.startswith("{") and '"roofline"' in line:
@@ -274,6 +319,23 @@ def measured_traffic(workload, key):
     if k is None or data["workload"] != workload or k["source_hash"] != source_hash(KERNELS[key][1]):
         return None
     return k["traffic_bytes"]
+
+
+def measured_counters(workload, key):
+    """MFMA busy, effective clock and LDS busy of one kernel from the committed SQ-counter
+    summary, or None when there is none for this workload or the kernel's sources
+    changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"sq_counters_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    data = json.loads(m.group(1))
+    k = data["kernels"].get(key)
+    if k is None or data["workload"] != workload or k["source_hash"] != source_hash(KERNELS[key][1]):
+        return None
+    return {f: k[f] for f in ("mfma_busy", "effective_clock_ghz", "lds_busy")}
 
 
 def step_flops(w, prob, ra, bounds=None):
@@ -497,6 +559,8 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    print("[bench] source hashes " + json.dumps({k: source_hash(f) for k, (_, f) in KERNELS.items()}),
+          file=sys.stderr, flush=True)
     import numpy as np
     import torch
 
@@ -658,6 +722,9 @@ def main():
                        "traffic": measured_traffic(w.name, name),
                        "kernel": name, "avg_launch_ms": round(launch_ms, 4),
                        "flop_per_launch": per_launch_flop}
+    counters = measured_counters(w.name, name)
+    if counters is not None:
+        res["roofline"]["counters"] = counters
     if res["roofline"]["traffic"] is not None:
         res["roofline"]["traffic_gbps"] = round(res["roofline"]["traffic"] / (launch_ms * 1e-3) / 1e9, 1)
     if not args.no_cpu_baseline:

@@ -1,4 +1,5 @@
 """Host-side logic of bench.py (no GPU): the one-GPU guard and the parity record."""
+import json
 import os
 import subprocess
 import sys
@@ -45,3 +46,32 @@ def test_sample_parity_passes_and_fails():
     ref, out, lse, dq = _fake(w, 40, 0.1)  # a 0.1 error in O breaks the bf16 gate
     res = bench.sample_parity(w, ref, out, lse, dq)
     assert not res["pass"] and res["o"]["max_abs"] > 0.05
+
+
+def test_counter_figures_only_for_the_sources_they_were_taken_on(tmp_path, monkeypatch):
+    key = "bwd_dkdv_kernel"
+    now = bench.source_hash(bench.KERNELS[key][1])
+    hashes = {k: bench.source_hash(f) for k, (_, f) in bench.KERNELS.items()}
+    log_a, log_b = tmp_path / "cnt_1.log", tmp_path / "cnt_2.log"
+    log_a.write_text("noise\n[bench] source hashes " + json.dumps(hashes) + "\n")
+    log_b.write_text("[bench] source hashes " + json.dumps(hashes) + "\n")
+    assert bench._logged_hashes(str(log_a), str(log_b)) == hashes
+    log_b.write_text("[bench] source hashes " + json.dumps({**hashes, key: "0" * 16}) + "\n")
+    assert bench._logged_hashes(str(log_a), str(log_b)) is None  # runs disagree
+    assert bench._logged_hashes(str(log_a), str(tmp_path / "missing.log")) is None
+
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    for stored, expect in ((now, True), ("f" * 16, False), (None, False)):
+        sq = {"workload": "zigzag_fwdbwd", "kernels": {key: {
+            "name": "bwd_dkdv_kernel", "source_hash": stored, "mfma_busy": 0.5,
+            "effective_clock_ghz": 2.0, "lds_busy": 0.4}}}
+        pmc = {"workload": "zigzag_fwdbwd", "kernels": {key: {
+            "name": "bwd_dkdv_kernel", "source_hash": stored, "traffic_bytes": 123.0}}}
+        (tmp_path / "sq_counters_zigzag_fwdbwd.md").write_text(
+            "# t\n\n```json\n" + json.dumps(sq) + "\n```\n")
+        (tmp_path / "pmc_traffic_zigzag_fwdbwd.md").write_text(
+            "# t\n\n```json\n" + json.dumps(pmc) + "\n```\n")
+        got_c = bench.measured_counters("zigzag_fwdbwd", key)
+        got_t = bench.measured_traffic("zigzag_fwdbwd", key)
+        assert (got_c is not None) == expect and (got_t is not None) == expect
+        assert bench.measured_counters("gqa_striped", key) is None  # other workload
