@@ -29,6 +29,13 @@ if ROOT not in sys.path:
 
 BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 F32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix
+# Vector ALU: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz = 39.3 T lane-operations/s for
+# full-rate fp32 instructions without the packed forms (exp and add have none).
+ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Vector operations the method needs per visible pair in every attention kernel: the
+# scaled shift of the score (one FMA), its exponential, and one more (the row sum in
+# the forward, the product P (dP - delta) in the backward).
+ALU_OPS_PER_PAIR = 3
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "ring_context_parallelism_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -299,8 +306,9 @@ def trace_summary(run_dir, workload):
                   f"{bench_line['fwd']['pct_peak']:.1f}% of peak"
                   + (f", backward {bench_line['bwd']['pct_peak']:.1f}%" if "bwd" in bench_line
                      else "")
-                  + f"; roofline kernel `{rf['kernel']}` {rf['avg_launch_ms']:.3f} ms per launch, "
-                  f"{rf['achieved']:.1f} TFLOP/s, frac {rf['frac']:.4f}."]
+                  + f"; roofline kernel `{rf['kernel']}` ({rf['bound']}-bound) "
+                  f"{rf['avg_launch_ms']:.3f} ms per launch, {rf['achieved']:.1f} {rf['unit']}, "
+                  f"frac {rf['frac']:.4f}."]
     lines.append("")
     return "\n".join(lines)
 
@@ -717,11 +725,22 @@ def main():
     name = max(kern, key=lambda k: kern[k][0])
     _, per_launch_flop, launch_ms = kern[name]
     achieved = per_launch_flop / (launch_ms * 1e-3) / 1e12
-    res["roofline"] = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                       "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                       "traffic": measured_traffic(w.name, name),
-                       "kernel": name, "avg_launch_ms": round(launch_ms, 4),
-                       "flop_per_launch": per_launch_flop}
+    # The kernel's binding roofline is the one it sits closer to: the matrix cores, or
+    # the vector ALU (small head dims, where the per-score softmax work dominates).
+    alu_ops = ALU_OPS_PER_PAIR * sum(pairs_bh) / len(steps)
+    alu_achieved = alu_ops / (launch_ms * 1e-3) / 1e12
+    if alu_achieved / ALU_PEAK_TOPS > achieved / peak:
+        res["roofline"] = {"bound": "alu", "achieved": round(alu_achieved, 3),
+                           "peak": round(ALU_PEAK_TOPS, 2), "unit": "TOP/s",
+                           "frac": round(alu_achieved / ALU_PEAK_TOPS, 4),
+                           "ops_per_launch": alu_ops, "mfma_frac": round(achieved / peak, 4)}
+    else:
+        res["roofline"] = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                           "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                           "flop_per_launch": per_launch_flop,
+                           "alu_frac": round(alu_achieved / ALU_PEAK_TOPS, 4)}
+    res["roofline"].update({"traffic": measured_traffic(w.name, name), "kernel": name,
+                            "avg_launch_ms": round(launch_ms, 4)})
     counters = measured_counters(w.name, name)
     if counters is not None:
         res["roofline"]["counters"] = counters
