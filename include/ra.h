@@ -216,10 +216,12 @@ ra_status_t ra_ring_bwd_workspace_size(const ra_problem_t* prob, size_t* bytes);
 
 /*
  * The ring driver, backward, for rank `rank`: runs ra_bwd_prepare (delta into
- * ws; dq and every dk_chunks[c], dv_chunks[c] zero-filled), then accumulates every
- * step with a visible pair.  out / lse are the forward's results for this rank.  dk_chunks and
- * dv_chunks are HOST arrays of p device pointers (fp32 [B, Hkv, L, D]); the result
- * is this rank's share of the gradients (its queries only).
+ * ws; dq and every dk_chunks[c], dv_chunks[c] zero-filled), then accumulates
+ * every step with a visible pair, in ring order.  out / lse are the forward's
+ * results for this rank.  dk_chunks and dv_chunks are HOST arrays of p device
+ * pointers (fp32 [B, Hkv, L, D]); the result is this rank's share of the
+ * gradients (its queries only).  ws: at least ra_ring_bwd_workspace_size()
+ * bytes, 256-byte aligned.  Supported: bf16.
  */
 ra_status_t ra_ring_bwd(const ra_problem_t* prob, int32_t rank, const void* q,
                         const void* const* k_chunks, const void* const* v_chunks,
