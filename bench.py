@@ -346,6 +346,24 @@ def measured_counters(workload, key):
     return {f: k[f] for f in ("mfma_busy", "effective_clock_ghz", "lds_busy")}
 
 
+def roofline(flop, pairs, launch_ms, mfma_peak):
+    """The roof a kernel sits closer to: the matrix cores (its algorithmic FLOP against
+    the dense MFMA peak of its dtype) or the vector ALU (ALU_OPS_PER_PAIR per visible
+    pair against ALU_PEAK_TOPS; small head dims, where the per-score softmax work
+    dominates).  The other fraction is reported alongside."""
+    achieved = flop / (launch_ms * 1e-3) / 1e12
+    alu_ops = ALU_OPS_PER_PAIR * pairs
+    alu_achieved = alu_ops / (launch_ms * 1e-3) / 1e12
+    if alu_achieved / ALU_PEAK_TOPS > achieved / mfma_peak:
+        return {"bound": "alu", "achieved": round(alu_achieved, 3),
+                "peak": round(ALU_PEAK_TOPS, 2), "unit": "TOP/s",
+                "frac": round(alu_achieved / ALU_PEAK_TOPS, 4), "ops_per_launch": alu_ops,
+                "mfma_frac": round(achieved / mfma_peak, 4)}
+    return {"bound": "mfma", "achieved": round(achieved, 3), "peak": mfma_peak,
+            "unit": "TFLOP/s", "frac": round(achieved / mfma_peak, 4), "flop_per_launch": flop,
+            "alu_frac": round(alu_achieved / ALU_PEAK_TOPS, 4)}
+
+
 def step_flops(w, prob, ra, bounds=None):
     """Algorithmic FLOP per live ring step: exact visible pairs x 4d (fwd), x 10d (bwd).
     Packed workloads count pairs inside documents (summed over the batch)."""
@@ -724,21 +742,7 @@ def main():
                                  q_ms / len(steps))
     name = max(kern, key=lambda k: kern[k][0])
     _, per_launch_flop, launch_ms = kern[name]
-    achieved = per_launch_flop / (launch_ms * 1e-3) / 1e12
-    # The kernel's binding roofline is the one it sits closer to: the matrix cores, or
-    # the vector ALU (small head dims, where the per-score softmax work dominates).
-    alu_ops = ALU_OPS_PER_PAIR * sum(pairs_bh) / len(steps)
-    alu_achieved = alu_ops / (launch_ms * 1e-3) / 1e12
-    if alu_achieved / ALU_PEAK_TOPS > achieved / peak:
-        res["roofline"] = {"bound": "alu", "achieved": round(alu_achieved, 3),
-                           "peak": round(ALU_PEAK_TOPS, 2), "unit": "TOP/s",
-                           "frac": round(alu_achieved / ALU_PEAK_TOPS, 4),
-                           "ops_per_launch": alu_ops, "mfma_frac": round(achieved / peak, 4)}
-    else:
-        res["roofline"] = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                           "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                           "flop_per_launch": per_launch_flop,
-                           "alu_frac": round(alu_achieved / ALU_PEAK_TOPS, 4)}
+    res["roofline"] = roofline(per_launch_flop, sum(pairs_bh) / len(steps), launch_ms, peak)
     res["roofline"].update({"traffic": measured_traffic(w.name, name), "kernel": name,
                             "avg_launch_ms": round(launch_ms, 4)})
     counters = measured_counters(w.name, name)

@@ -75,3 +75,17 @@ def test_counter_figures_only_for_the_sources_they_were_taken_on(tmp_path, monke
         got_t = bench.measured_traffic("zigzag_fwdbwd", key)
         assert (got_c is not None) == expect and (got_t is not None) == expect
         assert bench.measured_counters("gqa_striped", key) is None  # other workload
+
+
+def test_roofline_picks_the_closer_roof():
+    # d = 128, bf16: 4 d = 512 FLOP per pair against the matrix peak -- MFMA-bound
+    pairs = 3.436e10
+    r = bench.roofline(512 * pairs, pairs, 14.0, bench.BF16_PEAK_TFLOPS)
+    assert r["bound"] == "mfma" and abs(r["frac"] - 512 * pairs / 14e-3 / 1e12 / 2516.6) < 1e-4
+    assert r["alu_frac"] < r["frac"]
+    # d = 24: 96 FLOP per pair; the softmax's 3 vector operations per pair bind first
+    pairs = 2.8125e10
+    r = bench.roofline(96 * pairs, pairs, 4.6, bench.BF16_PEAK_TFLOPS)
+    assert r["bound"] == "alu" and r["unit"] == "TOP/s"
+    assert abs(r["achieved"] - 3 * pairs / 4.6e-3 / 1e12) < 1e-2
+    assert abs(bench.ALU_PEAK_TOPS - 39.3216) < 1e-3 and r["mfma_frac"] < r["frac"]
