@@ -1,5 +1,5 @@
 // Forward ring step: one query chunk against one KV chunk, tiled online softmax
-// with an fused LSE-merge epilogue.
+// with a fused LSE-merge epilogue.
 //
 // What it computes ("Ring Attention & Friends", "Flash Attention - Tiling with the
 // Softmax Rescaling Trick"; Mosaic post, "How Ring Attention Works"): for every query
