@@ -1,4 +1,5 @@
-"""The ring drivers under HIP graph capture, and run-to-run determinism.
+"""The ring drivers under HIP graph capture, run-to-run determinism, and two ring
+steps running at once on two streams.
 
 The library allocates nothing and clears buffers with its own fill kernel (no
 memset nodes), so a caller can capture a whole ring step into a graph.  The test
@@ -90,3 +91,35 @@ def test_ring_backward_is_deterministic():
         torch.cuda.synchronize()
         for a, b in zip([again[0]] + again[1] + again[2], first):
             assert torch.equal(a, b)
+
+
+def test_ring_steps_on_two_streams_are_independent():
+    """Two ring steps of different problems run at once on two streams (default
+    priority) give bit for bit the results each gives alone: the library keeps no
+    state between calls."""
+    dev = need_gpu()
+    wa = _wl()
+    wb = Workload("graph_b", 601, "bf16", 1, 4, 1, 64, 64, 900, 3, "striped", 1, True,
+                  "normal", 0.5, backward=True)
+    shares = [staging.stage(w, generate(w), dev, rank=w.rank) for w in (wa, wb)]
+    alone = []
+    for w, sh in zip((wa, wb), shares):
+        out, lse = staging.ring_forward(sh, w, rank=w.rank)
+        dq, dks, dvs = staging.ring_backward(sh, w, out, lse, rank=w.rank)
+        torch.cuda.synchronize()
+        alone.append([out.clone(), lse.clone(), dq.clone()] + [x.clone() for x in dks + dvs])
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        say(f"two streams, repetition {rep}")
+        got = [None, None]
+        for i, (w, sh, s) in enumerate(zip((wa, wb), shares, streams)):
+            with torch.cuda.stream(s):
+                out, lse = staging.ring_forward(sh, w, rank=w.rank)
+                dq, dks, dvs = staging.ring_backward(sh, w, out, lse, rank=w.rank)
+                got[i] = [out, lse, dq] + dks + dvs
+        torch.cuda.synchronize()
+        for g, a in zip(got, alone):
+            for x, y in zip(g, a):
+                assert torch.equal(x, y)
