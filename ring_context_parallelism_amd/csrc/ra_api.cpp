@@ -152,7 +152,7 @@ ra::FwdArgs fwd_args(const ra_problem_t* p, const void* q, int cq, const void* k
   a.ck = ck;
   a.causal = p->causal;
   a.map = make_map(p);
-  const int bm = ra::fwd_block_m(p->dtype, (int)p->head_dim_padded);
+  const int bm = ra::fwd_block_m(p->dtype, (int)p->head_dim_padded, p->seg_bounds != nullptr);
   a.n_qtiles = (a.map.L + bm - 1) / bm;
   a.scale_log2 = softmax_scale(p) * 1.4426950408889634f;
   a.seg = p->seg_bounds;

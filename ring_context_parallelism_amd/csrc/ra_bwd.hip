@@ -467,12 +467,21 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------- dQ kernel
 
-constexpr int kQThreads = 512;  // 8 waves
-constexpr int kQBM = 256;       // query rows per workgroup
+// Workgroup shape of the dQ kernel: 8 waves (256 query rows, each K/V tile serving
+// all of them) on dense sequences; 4 waves (128 rows, two workgroups per CU) with
+// packed documents, where fewer workgroups straddle a document boundary (6% faster
+// there, 2% slower on dense sequences).
+template <bool PACKED>
+struct QCfg {
+  static constexpr int NT = PACKED ? 256 : 512;  // threads
+  static constexpr int BM = PACKED ? 128 : 256;  // query rows per workgroup
+};
 constexpr int kQBN = 32;        // keys per KV tile
 
 template <int D, bool PACKED>
-__global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__((QCfg<PACKED>::NT), (PACKED ? 2 : 1)) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int kQThreads = QCfg<PACKED>::NT;
+  constexpr int kQBM = QCfg<PACKED>::BM;
   constexpr int NKK = D / 32;  // 32-wide head-dim steps of the S^T and dP^T contractions
   constexpr int NDT = D / 16;  // 16-row head-dim tiles of dQ^T
   using PK = Pad<D>;
@@ -684,8 +693,8 @@ hipError_t launch(const BwdArgs& a, int which, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (which & 2) {
-    const int64_t nq = (int64_t)a.B * a.Hq * ((a.map.L + kQBM - 1) / kQBM);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, PK>), dim3((unsigned)nq), dim3(kQThreads), 0, s, a);
+    const int64_t nq = (int64_t)a.B * a.Hq * ((a.map.L + QCfg<PK>::BM - 1) / QCfg<PK>::BM);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, PK>), dim3((unsigned)nq), dim3(QCfg<PK>::NT), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -39,10 +39,12 @@ constexpr int kBM = 32 * kWaves;
 
 // Waves per bf16 workgroup (32 query rows each).  At D = 128 a workgroup of 8 waves
 // (256 rows) shares each K/V tile between twice the rows, which measured 2-6% faster
-// than 4 waves; at D = 32 the 4-wave workgroup is faster.
-template <int D>
+// than 4 waves on dense sequences; with packed documents the 4-wave workgroup is
+// faster (fewer workgroups straddle a document boundary, whose rows then see
+// disjoint key ranges), and at D = 32 it is faster too.
+template <int D, bool PK>
 struct Bf16Cfg {
-  static constexpr int NW = D == 128 ? 8 : 4;
+  static constexpr int NW = (D == 128 && !PK) ? 8 : 4;
   static constexpr int NT = 64 * NW;  // threads
   static constexpr int BM = 32 * NW;  // query rows
 };
@@ -282,10 +284,10 @@ __device__ inline void fwd_epilogue16(const FwdArgs& a, int b, int h, int tq, in
 }
 
 template <int D, int BN, bool PK>
-__global__ __launch_bounds__(Bf16Cfg<D>::NT, Bf16Cfg<D>::NW == 8 ? 1 : 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__((Bf16Cfg<D, PK>::NT), (Bf16Cfg<D, PK>::NW == 8 ? 1 : 2)) void fwd_bf16_kernel(
     FwdArgs a) {
-  constexpr int kBM = Bf16Cfg<D>::BM;
-  constexpr int NT = Bf16Cfg<D>::NT;
+  constexpr int kBM = Bf16Cfg<D, PK>::BM;
+  constexpr int NT = Bf16Cfg<D, PK>::NT;
   constexpr int NKK = D / 32;   // 32-wide head-dim steps of the QK^T contraction
   constexpr int NDT = D / 16;   // 16-row head-dim tiles of O^T
   constexpr int NKT = BN / 16;  // 16-key tiles per KV tile
@@ -653,17 +655,18 @@ hipError_t launch_grid(K kernel, const FwdArgs& a, int threads, hipStream_t s) {
 
 }  // namespace
 
-int fwd_block_m(int dtype, int D) {
+int fwd_block_m(int dtype, int D, bool packed) {
   if (dtype != RA_BF16) return kBM;
-  return D == 128 ? Bf16Cfg<128>::BM : (D == 64 ? Bf16Cfg<64>::BM : Bf16Cfg<32>::BM);
+  if (packed) return D == 128 ? Bf16Cfg<128, true>::BM : (D == 64 ? Bf16Cfg<64, true>::BM : Bf16Cfg<32, true>::BM);
+  return D == 128 ? Bf16Cfg<128, false>::BM : (D == 64 ? Bf16Cfg<64, false>::BM : Bf16Cfg<32, false>::BM);
 }
 
 template <bool PK>
 hipError_t launch_fwd_t(int dtype, int D, const FwdArgs& a, hipStream_t s) {
   if (dtype == RA_BF16) {
-    if (D == 128) return launch_grid(fwd_bf16_kernel<128, 64, PK>, a, Bf16Cfg<128>::NT, s);
-    if (D == 64) return launch_grid(fwd_bf16_kernel<64, 64, PK>, a, Bf16Cfg<64>::NT, s);
-    if (D == 32) return launch_grid(fwd_bf16_kernel<32, 64, PK>, a, Bf16Cfg<32>::NT, s);
+    if (D == 128) return launch_grid(fwd_bf16_kernel<128, 64, PK>, a, Bf16Cfg<128, PK>::NT, s);
+    if (D == 64) return launch_grid(fwd_bf16_kernel<64, 64, PK>, a, Bf16Cfg<64, PK>::NT, s);
+    if (D == 32) return launch_grid(fwd_bf16_kernel<32, 64, PK>, a, Bf16Cfg<32, PK>::NT, s);
   } else {
     if (D == 128) return launch_grid(fwd_f32_kernel<128, 32, PK>, a, kThreads, s);
     if (D == 64) return launch_grid(fwd_f32_kernel<64, 64, PK>, a, kThreads, s);
