@@ -42,13 +42,21 @@ PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_BYTES = 1 << 30
 # kernel key -> (substring of the device function's name, sources it is built from)
 WARM_SECONDS = 0.5  # default untimed warmup work, seconds
+DEFAULT_WORKLOAD = "zigzag_fwdbwd"
+# The forward-only workloads the default run also times (each as one object of the
+# line's "configs" list), in the order of their sizes.
+OTHER_CONFIGS = ("tiny_fp32", "llama_share", "gqa_striped", "tabular_rows", "tabular_rows_bf16")
 
 KERNELS = {
     "fwd_kernel": ("fwd_bf16_kernel", ("ra_fwd.hip", "ra_internal.h")),
     "fwd_kernel_f32": ("fwd_f32_kernel", ("ra_fwd.hip", "ra_internal.h")),
     "bwd_dkdv_kernel": ("bwd_dkdv_kernel", ("ra_bwd.hip", "ra_internal.h")),
     "bwd_dq_kernel": ("bwd_dq_kernel", ("ra_bwd.hip", "ra_internal.h")),
+    "lse_merge_kernel": ("lse_merge_kernel", ("ra_misc.hip", "ra_internal.h")),
+    "bwd_delta_kernel": ("bwd_delta_kernel", ("ra_misc.hip", "ra_internal.h")),
 }
+# Shapes the HBM-bound helpers are timed and counted at (--aux): (name, rows, head dim).
+AUX_SHAPES = {"llama_share": (1 * 16 * 8192, 128), "zigzag_fwdbwd": (16 * 65536, 128)}
 
 
 def parse():
@@ -59,9 +67,11 @@ def parse():
                     help="untimed warmup steps (default: at least 2, and enough for about "
                          f"{WARM_SECONDS} s of work, so that short workloads run at the "
                          "clock a sustained load settles at)")
-    ap.add_argument("--workload", default="zigzag_fwdbwd")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--dtype", default=None, help="override the workload dtype (f32|bf16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the forward-only workloads timed after the default one")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -70,6 +80,8 @@ def parse():
     ap.add_argument("--aux", action="store_true",
                     help="time the HBM-bound helper kernels (standalone LSE merge, delta) "
                          "instead of the step and print one JSON line")
+    ap.add_argument("--aux-shape", default=None, choices=sorted(AUX_SHAPES),
+                    help="with --aux: only this shape (one shape per counter run)")
     ap.add_argument("--sq-summary", metavar="DIR", default=None,
                     help="print the markdown summary of the three SQ-counter --pmc runs under "
                          "DIR (cnt_1/, cnt_2/, cnt_3/) and exit")
@@ -130,6 +142,22 @@ def _counter_kib(run_dir, counter):
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
 
+def _profiled_args(workload):
+    """bench.py arguments of a counter run: one step of the workload, or the helper
+    kernels at the zig-zag share's shape for the pseudo-workload "aux"."""
+    if workload == "aux":
+        return "--aux --aux-shape zigzag_fwdbwd"
+    return f"--workload {workload} --steps 1 --warmup 0 --no-cpu-baseline --no-configs"
+
+
+def _aux_algorithmic_bytes(workload):
+    """Algorithmic bytes per launch of the helper kernels of an "aux" counter run."""
+    if workload != "aux":
+        return {}
+    rows, d = AUX_SHAPES["zigzag_fwdbwd"]
+    return {"lse_merge_kernel": rows * (3 * d + 3) * 4, "bwd_delta_kernel": rows * (2 * d * 2 + 4)}
+
+
 def pmc_summary(root, workload):
     """Traffic per dispatch from FETCH_SIZE and WRITE_SIZE, each scaled by what the same
     counter reads for a plain device copy of COPY_PROBE_BYTES."""
@@ -143,12 +171,11 @@ def pmc_summary(root, workload):
     w_factor = COPY_PROBE_BYTES / (cw[copy_name][0] * 1024.0)
     cmd = ("cd /tmp && timeout -s KILL 240 rocprofv3 --pmc {c} --output-format csv -d <out>/{d} "
            "-o run -- python3 <repo>/bench.py {a}")
+    run_args = _profiled_args(workload)
     lines = [f"# HBM traffic per dispatch: {workload} workload", "",
              "Commands (one counter per run, on one MI355X):", "", "```"]
-    for c, d, a in (("FETCH_SIZE", "pmc_fetch", f"--workload {workload} --steps 1 --warmup 0 "
-                     "--no-cpu-baseline"),
-                    ("WRITE_SIZE", "pmc_write", f"--workload {workload} --steps 1 --warmup 0 "
-                     "--no-cpu-baseline"),
+    for c, d, a in (("FETCH_SIZE", "pmc_fetch", run_args),
+                    ("WRITE_SIZE", "pmc_write", run_args),
                     ("FETCH_SIZE", "pmc_copy_fetch", f"--copy-probe {COPY_PROBE_BYTES}"),
                     ("WRITE_SIZE", "pmc_copy_write", f"--copy-probe {COPY_PROBE_BYTES}")):
         lines.append(cmd.format(c=c, d=d, a=a))
@@ -160,6 +187,7 @@ def pmc_summary(root, workload):
               "written (GB) | traffic (GB) |", "|---|---|---|---|---|---|---|"]
     logged = _logged_hashes(os.path.join(root, "pmc_fetch.log"), os.path.join(root, "pmc_write.log")) or {}
     data = {"workload": workload, "fetch_factor": f_factor, "write_factor": w_factor, "kernels": {}}
+    algo = _aux_algorithmic_bytes(workload)
     for key, (sub, files) in KERNELS.items():
         name = next((k for k in fetch if sub in k), None)
         if name is None or name not in write:
@@ -168,9 +196,18 @@ def pmc_summary(root, workload):
         wb = write[name][0] * 1024.0 * w_factor
         data["kernels"][key] = {"name": name, "source_hash": logged.get(key),
                                 "fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb}
+        if key in algo:
+            data["kernels"][key].update(algorithmic_bytes=algo[key],
+                                        traffic_over_algorithmic=(fb + wb) / algo[key])
         lines.append(f"| `{name[:80]}` | {fetch[name][1]} | {fetch[name][0]:.0f} | "
                      f"{write[name][0]:.0f} | {fb / 1e9:.3f} | {wb / 1e9:.3f} | "
                      f"{(fb + wb) / 1e9:.3f} |")
+    if algo:
+        lines += ["", "Algorithmic bytes per launch at this shape (merge: (3 d + 3) x 4 B per "
+                  "row; delta: 2 d x 2 B + 4 B per row): "
+                  + "; ".join(f"`{k}` {v / 1e9:.3f} GB (measured / algorithmic = "
+                              f"{data['kernels'][k]['traffic_over_algorithmic']:.3f})"
+                              for k, v in algo.items() if k in data["kernels"]) + "."]
     lines += ["", "Source hashes (sha256 prefix of the kernel's source files, as printed by the "
               "profiled bench runs) identify the kernel build the counters were taken on; "
               "`bench.py` reports `traffic` only while they match.", "", "```json",
@@ -203,10 +240,10 @@ def sq_summary(root, workload, n_cu=256):
                 dur.setdefault(key, {})[(i, r["Dispatch_Id"])] = (
                     int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
     cmd = ("cd /tmp && timeout -s KILL 200 rocprofv3 --pmc {c} --output-format csv -d <out>/cnt_{i} "
-           "-o run -- python3 <repo>/bench.py --workload {w} --steps 1 --warmup 0 --no-cpu-baseline")
+           "-o run -- python3 <repo>/bench.py {a}")
     lines = [f"# SQ counters per kernel: {workload} workload", "",
              "Commands (three passes, at most 8 SQ counters each, on one MI355X):", "", "```"]
-    lines += [cmd.format(c=c, i=i + 1, w=workload) for i, c in enumerate(SQ_PASSES)]
+    lines += [cmd.format(c=c, i=i + 1, a=_profiled_args(workload)) for i, c in enumerate(SQ_PASSES)]
     lines += ["python3 <repo>/bench.py --sq-summary <out>", "```", "",
               "Cycle counters are summed over the chip (`SQ_BUSY_CU_CYCLES` over 256 CUs, "
               "`SQ_VALU_MFMA_BUSY_CYCLES` over 1024 SIMDs; the latter counts the clocks each "
@@ -247,69 +284,98 @@ def sq_summary(root, workload, n_cu=256):
     return "\n".join(lines)
 
 
+def _problem_of(w, bounds=None):
+    """ra_problem_t of a workload for the host-only calls (pair counts): a packed
+    workload gets a stand-in boundary address, which these calls never read."""
+    from ring_context_parallelism_amd import ra
+    kw = {} if bounds is None else dict(seg_bounds=1 << 20, seg_count=int(bounds.shape[1]))
+    return ra.make_problem(batch=w.batch, heads_q=w.heads_q, heads_kv=w.heads_kv,
+                           head_dim=w.head_dim, head_dim_padded=w.head_dim_padded,
+                           seq_total=w.seq_total, world=w.world, layout=w.layout,
+                           causal=w.causal, dtype=w.dtype, **kw)
+
+
+def _bench_line(log):
+    if os.path.exists(log):
+        for line in open(log):
+            if line.startswith("{") and '"roofline"' in line:
+                return json.loads(line)
+    return None
+
+
 def trace_summary(run_dir, workload):
-    """Kernel durations from a --kernel-trace --stats run, with the algorithmic FLOP rate of
-    each attention kernel (forward 4d, dK/dV 8d, dQ 2d per visible pair and head)."""
+    """Kernel durations from a --kernel-trace run, with the algorithmic FLOP rate of each
+    attention kernel (forward 4d, dK/dV 8d, dQ 2d per visible pair and head) over the
+    launches of the timed steps only: the warmup steps before them and the forward's
+    per-step timing pass after them are left out."""
+    import numpy as np
+
     from ring_context_parallelism_amd import ra
     from ring_context_parallelism_amd.workloads import WORKLOADS, document_bounds
     w = WORKLOADS[workload]
     bounds = document_bounds(w) if w.docs else None
-    prob = ra.make_problem(batch=w.batch, heads_q=w.heads_q, heads_kv=w.heads_kv,
-                           head_dim=w.head_dim, head_dim_padded=w.head_dim_padded,
-                           seq_total=w.seq_total, world=w.world, layout=w.layout,
-                           causal=w.causal, dtype=w.dtype)
-    steps = step_flops(w, prob, ra, bounds)
-    pairs = sum(st["visible_pairs_per_head"] * w.batch * w.heads_q for st in steps) / len(steps)
-    per_pair = {"fwd_bf16_kernel": 4, "fwd_f32_kernel": 4, "bwd_dkdv_kernel": 8,
-                "bwd_dq_kernel": 2}
+    steps = step_flops(w, _problem_of(w, bounds), ra, bounds)
+    n_live = len(steps)
+    pairs = sum(st["visible_pairs_per_head"] * w.batch * w.heads_q for st in steps) / n_live
+    per_pair = {"fwd_kernel": 4, "fwd_kernel_f32": 4, "bwd_dkdv_kernel": 8, "bwd_dq_kernel": 2}
     peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
-    rows = list(csv.DictReader(open(os.path.join(run_dir, "run_kernel_stats.csv"))))
-    bench_line = None
     log = run_dir.rstrip("/") + ".log"
     _check_workload(log, workload)
-    if os.path.exists(log):
-        for line in open(log):
-            if line.startswith("{") and '"roofline"' in line:
-                bench_line = json.loads(line)
-    lines = [f"# Kernel durations: {workload} workload ({w.batch} x {w.heads_q} heads x "
-             f"d{w.head_dim}, S={w.seq_total}, {w.layout} p={w.world}, rank {w.rank}, {w.dtype})",
+    bench_line = _bench_line(log)
+    if bench_line is None:
+        raise SystemExit(f"bench.py: no bench line in {log}")
+    warm, timed = int(bench_line["warmup"]), int(bench_line["steps"])
+    launches = {}
+    for r in csv.DictReader(open(os.path.join(run_dir, "run_kernel_trace.csv"))):
+        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        launches.setdefault(r["Kernel_Name"], []).append((t0, (t1 - t0) * 1e-6))
+    total = sum(d for xs in launches.values() for _, d in xs)
+    lines = [f"# Kernel durations: {workload} workload ({w.batch} x {w.heads_q}/{w.heads_kv} heads "
+             f"x d{w.head_dim}, S={w.seq_total}, {w.layout} p={w.world}, rank {w.rank}, {w.dtype}"
+             f"{', packed documents' if w.docs else ''})",
              "", "Command (run from /tmp on one MI355X):", "", "```",
              "cd /tmp && timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv "
-             "-d <out>/prof_default -o run -- python3 <repo>/bench.py --workload "
-             f"{workload} --steps 3 --warmup 1 --no-cpu-baseline > <out>/prof_default.log",
-             f"python3 <repo>/bench.py --workload {workload} --trace-summary <out>/prof_default",
+             "-d <out>/prof_" + workload + " -o run -- python3 <repo>/bench.py --workload "
+             f"{workload} --steps {timed} --warmup {warm} --no-cpu-baseline --no-configs > "
+             f"<out>/prof_{workload}.log",
+             f"python3 <repo>/bench.py --workload {workload} --trace-summary <out>/prof_{workload}",
              "```", "",
-             f"{len(steps)} live ring steps per bench step; {pairs:.4g} visible (query, key) pairs "
-             "per launch summed over batch and heads.  Algorithmic FLOP per launch: forward 4d, "
-             "dK/dV kernel 8d (S, dP, dV, dK), dQ kernel 2d (its recomputation of S and dP is "
-             "not counted) per pair.  The forward kernel's calls include the per-step "
-             "timing pass that follows the timed steps (each live step launched once more "
-             "on its own).", "",
-             "| kernel | calls | average (ms) | min (ms) | max (ms) | share | algorithmic "
-             "TFLOP/s | of peak |", "|---|---|---|---|---|---|---|---|"]
-    for r in rows:
-        avg = float(r["AverageNs"]) * 1e-6
-        rate = ""
-        frac = ""
-        for sub, k in per_pair.items():
-            if sub in r["Name"]:
-                tf = k * w.head_dim * pairs / (avg * 1e-3) / 1e12
-                rate, frac = f"{tf:.1f}", f"{100 * tf / peak:.1f}%"
-        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {avg:.3f} | "
-                     f"{float(r['MinNs']) * 1e-6:.3f} | {float(r['MaxNs']) * 1e-6:.3f} | "
-                     f"{float(r['Percentage']):.2f}% | {rate} | {frac} |")
-    if bench_line is not None:
-        rf = bench_line["roofline"]
-        lines += ["", "The bench line printed by the same profiled command (HIP events on the "
-                  "launch stream, timed steps only; the rocprof averages include the warmup "
-                  f"step): {bench_line['value']:.1f} TFLOP/s per step, forward "
-                  f"{bench_line['fwd']['pct_peak']:.1f}% of peak"
-                  + (f", backward {bench_line['bwd']['pct_peak']:.1f}%" if "bwd" in bench_line
-                     else "")
-                  + f"; roofline kernel `{rf['kernel']}` ({rf['bound']}-bound) "
-                  f"{rf['avg_launch_ms']:.3f} ms per launch, {rf['achieved']:.1f} {rf['unit']}, "
-                  f"frac {rf['frac']:.4f}."]
-    lines.append("")
+             f"{n_live} live ring steps per bench step; {pairs:.4g} visible (query, key) pairs "
+             "per launch (mean over the live steps) summed over batch and heads.  Algorithmic "
+             "FLOP per launch: forward 4d, dK/dV kernel 8d (S, dP, dV, dK), dQ kernel 2d (its "
+             "recomputation of S and dP is not counted) per pair.  The attention kernels' "
+             f"figures cover the {timed} timed steps only ({timed * n_live} launches each): the "
+             f"{warm} warmup step(s) before them and the forward's per-step timing pass after "
+             "them are left out.  Other kernels: every launch.", "",
+             "| kernel | launches (all) | timed launches | mean (ms) | median (ms) | min (ms) | "
+             "max (ms) | share of GPU time | algorithmic TFLOP/s (mean) | of peak |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    data = {"workload": workload, "kernels": {}}
+    for name, xs in sorted(launches.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        durs = [d for _, d in sorted(xs)]
+        key = next((k for k in per_pair if KERNELS[k][0] in name), None)
+        sel = durs[warm * n_live:(warm + timed) * n_live] if key else durs
+        if not sel:
+            continue
+        mean, med = float(np.mean(sel)), float(np.median(sel))
+        rate = frac = ""
+        if key:
+            tf = per_pair[key] * w.head_dim * pairs / (mean * 1e-3) / 1e12
+            rate, frac = f"{tf:.1f}", f"{100 * tf / peak:.1f}%"
+            data["kernels"][key] = {"name": name, "timed_launches": len(sel), "mean_ms": mean,
+                                    "median_ms": med, "tflops": tf, "frac": tf / peak}
+        lines.append(f"| `{name[:90]}` | {len(durs)} | {len(sel)} | {mean:.3f} | {med:.3f} | "
+                     f"{min(sel):.3f} | {max(sel):.3f} | {100 * sum(durs) / total:.2f}% | "
+                     f"{rate} | {frac} |")
+    rf = bench_line["roofline"]
+    lines += ["", "The bench line printed by the same profiled command (HIP events on the "
+              f"launch stream, the same timed steps): {bench_line['value']:.1f} TFLOP/s per "
+              f"step, forward {bench_line['fwd']['pct_peak']:.1f}% of peak"
+              + (f", backward {bench_line['bwd']['pct_peak']:.1f}%" if "bwd" in bench_line
+                 else "")
+              + f"; roofline kernel `{rf['kernel']}` ({rf['bound']}-bound) "
+              f"{rf['avg_launch_ms']:.3f} ms per launch, {rf['achieved']:.1f} {rf['unit']}, "
+              f"frac {rf['frac']:.4f}.", "", "```json", json.dumps(data, indent=1), "```", ""]
     return "\n".join(lines)
 
 
@@ -384,65 +450,112 @@ def step_flops(w, prob, ra, bounds=None):
     return out
 
 
-def cpu_baseline(w, arrays, target_s):
-    """The oracle, as it is, on a bounded sample of the same share (fp64, host cores)."""
+def _blas_name():
+    try:
+        from threadpoolctl import threadpool_info
+        return ",".join(sorted({p.get("internal_api", "?") for p in threadpool_info()})) or "?"
+    except Exception:  # pragma: no cover - reporting only
+        return "unknown"
+
+
+def _pairs_of_rows(w, rows, bounds):
+    """Exact visible (query, key) pairs of the given global query rows, per head, summed
+    over the batch (the oracle's own arithmetic is not used: this only prices its work)."""
+    import numpy as np
+    if bounds is None:
+        per = float(np.sum(rows + 1)) if w.causal else float(rows.size * w.seq_total)
+        return per * w.batch
+    pairs = 0.0
+    for e in bounds:
+        e = np.asarray(e, dtype=np.int64)
+        k = np.searchsorted(e, rows, side="right") - 1
+        live = rows < e[-1]
+        start, end = e[np.clip(k, 0, e.size - 1)], e[np.clip(k + 1, 0, e.size - 1)]
+        cnt = np.where(w.causal, rows - start + 1, end - start)
+        pairs += float(np.sum(np.where(live, cnt, 0)))
+    return pairs
+
+
+def cpu_baseline(w, arrays, target_s, full_bwd_max_s=120.0):
+    """The oracle, as it is, on a bounded sample of the same share (fp64, host cores).
+
+    The oracle's rows are spread over a pool of threads, one BLAS thread each
+    (oracle.rows).  Forward workloads: a sample of head 0's rows, grown until it takes
+    about 0.6 x target_s.  Backward workloads: the whole of head 0 forward + backward
+    (dQ of every row, dK and dV of every key) when a calibration run projects it
+    within full_bwd_max_s, else a row sample; then O and LSE on a row sample.
+    Returns (record, reference values for sample_parity)."""
     import numpy as np
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        blas = ",".join(sorted({p.get("internal_api", "?") for p in threadpool_info()}))
-    except Exception:  # pragma: no cover - reporting only
-        threads, blas = 1, "unknown"
+    from oracle.rows import attention_bwd_rows, attention_fwd_rows, default_workers
+    workers = default_workers()
     rows_all = oracle.positions(w.layout, w.seq_total, w.world, w.rank)
     bounds = None if arrays.get("bounds") is None else [list(map(int, e)) for e in arrays["bounds"]]
     rng = np.random.default_rng(1234)
+    d = w.head_dim
+    total_s, flop, what = 0.0, 0.0, []
+    ref = {"head": 0}
+
+    def fwd(t_idx):
+        t0 = time.perf_counter()
+        O, LSE = attention_fwd_rows(arrays["q"], arrays["k"], arrays["v"], rows_all[t_idx],
+                                    w.causal, heads=[0], bounds=bounds, workers=workers)
+        return (O, LSE), time.perf_counter() - t0
+
+    def bwd(t_idx):
+        rows = rows_all[t_idx]
+        t0 = time.perf_counter()
+        g = attention_bwd_rows(arrays["q"], arrays["k"], arrays["v"],
+                               arrays["do"][:, :1][:, :, rows], rows, w.causal, heads=[0],
+                               bounds=bounds, workers=workers)
+        return g, time.perf_counter() - t0
+
+    fwd_share = 0.6
+    if w.backward:
+        # calibration sample, then the whole head when it fits the time bound
+        b_idx = np.sort(rng.choice(rows_all.size, size=min(1024, rows_all.size), replace=False))
+        grads, dt = bwd(b_idx)
+        projected = dt * _pairs_of_rows(w, rows_all, bounds) / max(
+            _pairs_of_rows(w, rows_all[b_idx], bounds), 1.0)
+        whole = projected <= full_bwd_max_s
+        if whole:
+            b_idx = np.arange(rows_all.size)
+            grads, dt = bwd(b_idx)
+        total_s += dt
+        flop += 14.0 * d * _pairs_of_rows(w, rows_all[b_idx], bounds)
+        what.append(f"{'every query row' if whole else f'{b_idx.size} query rows'} of head 0, "
+                    f"forward + backward ({dt:.1f} s)")
+        ref.update(bwd_idx=b_idx, dQ=grads[0], dK=grads[1] if whole else None,
+                   dV=grads[2] if whole else None)
+        fwd_share = 0.2
     n = 64
     while True:
         t_idx = np.sort(rng.choice(rows_all.size, size=min(n, rows_all.size), replace=False))
-        rows = rows_all[t_idx]
-        t0 = time.perf_counter()
-        dQ = None
-        if w.backward:
-            dO = arrays["do"][:, :1][:, :, rows]
-            dQ, _, _ = oracle.attention_bwd(arrays["q"], arrays["k"], arrays["v"], dO, rows,
-                                            w.causal, heads=[0], bounds=bounds)
-        O, LSE = oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal,
-                                      heads=[0], bounds=bounds)
-        dt = time.perf_counter() - t0
-        if dt >= 0.6 * target_s or n >= rows_all.size:
+        (O, LSE), dt = fwd(t_idx)
+        budget = fwd_share * target_s
+        if dt >= budget or n >= rows_all.size:
             break
-        # grow the sample towards the target wall time (at most 16x per round)
-        n = int(min(rows_all.size, n * min(16.0, max(2.0, target_s / max(dt, 1e-3)))))
-    if bounds is None:
-        pairs = float(np.sum(rows + 1)) if w.causal else float(rows.size * w.seq_total)
-    else:  # keys of the row's own document (at or before it when causal), per batch element
-        pairs = 0.0
-        for e in bounds:
-            e = np.asarray(e, dtype=np.int64)
-            k = np.searchsorted(e, rows, side="right") - 1
-            live = rows < e[-1]
-            start, end = e[np.clip(k, 0, e.size - 1)], e[np.clip(k + 1, 0, e.size - 1)]
-            cnt = np.where(w.causal, rows - start + 1, end - start)
-            pairs += float(np.sum(np.where(live, cnt, 0)))
-        pairs /= w.batch
-    per_pair = (4.0 + (10.0 if w.backward else 0.0)) * w.head_dim
-    flop = pairs * per_pair * w.batch
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{rows.size} query rows of head 0 (batch {w.batch}), "
-                      f"{'forward + backward' if w.backward else 'forward'} in fp64, "
-                      f"{pairs:.3e} visible pairs, {dt:.1f} s wall, BLAS {blas}",
-            "seconds": dt}, (t_idx, O, LSE, dQ)
+        n = int(min(rows_all.size, n * min(16.0, max(2.0, budget / max(dt, 1e-3)))))
+    total_s += dt
+    flop += 4.0 * d * _pairs_of_rows(w, rows_all[t_idx], bounds)
+    what.append(f"{t_idx.size} query rows of head 0, forward ({dt:.1f} s)")
+    ref.update(fwd_idx=t_idx, O=O, LSE=LSE)
+    host_cores = len(os.sched_getaffinity(0))
+    rec = {"value": flop / total_s / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+           "sample": "; ".join(what) + f" in fp64 (batch {w.batch}), {flop:.3e} algorithmic "
+                     f"FLOP in {total_s:.1f} s",
+           "pool": f"{workers} worker threads, 1 BLAS thread each ({_blas_name()})",
+           "host_cores": host_cores, "seconds": total_s}
+    return rec, ref
 
 
-def sample_parity(w, ref, out, lse, dq):
-    """The timed run's outputs on the oracle's sample rows (head 0) against the oracle."""
+def sample_parity(w, ref, out, lse, dq=None, dks=None, dvs=None):
+    """The timed run's outputs against the oracle's: O and LSE on the sampled rows of
+    head 0; dQ on the rows the oracle's backward covered; dK and dV of every key of
+    every chunk for head 0's KV head when the oracle ran the whole head."""
     import numpy as np
-    t_idx, O, LSE, dQ = ref
     d = w.head_dim
-    ti = torch_index(t_idx, out.device)
 
     def cmp(got, want):
         err = np.abs(got - want)
@@ -450,17 +563,32 @@ def sample_parity(w, ref, out, lse, dq):
         return {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
                 "rel_fro": float(np.linalg.norm(got - want) / den) if den > 0 else 0.0}
 
-    res = {"rows": int(t_idx.size), "head": 0}
-    res["o"] = cmp(out[:, :1][:, :, ti].float().cpu().numpy()[..., :d], O)
+    ti = torch_index(ref["fwd_idx"], out.device)
+    res = {"rows": int(ref["fwd_idx"].size), "head": 0}
+    res["o"] = cmp(out[:, :1][:, :, ti].float().cpu().numpy()[..., :d], ref["O"])
     lg = lse[:, :1][:, :, ti].cpu().numpy()
+    LSE = ref["LSE"]
     fin = np.isfinite(LSE)
     res["lse_max_abs"] = float(np.abs(lg[fin] - LSE[fin]).max()) if fin.any() else 0.0
     res["lse_inf_rows_match"] = bool(np.array_equal(np.isneginf(lg), np.isneginf(LSE)))
-    if dQ is not None and dq is not None:
-        res["dq"] = cmp(dq[:, :1][:, :, ti].cpu().numpy()[..., :d], dQ)
+    if ref.get("dQ") is not None and dq is not None:
+        bi = torch_index(ref["bwd_idx"], dq.device)
+        res["bwd_rows"] = int(ref["bwd_idx"].size)
+        res["dq"] = cmp(dq[:, :1][:, :, bi].cpu().numpy()[..., :d], ref["dQ"])
+    if ref.get("dK") is not None and dks is not None:
+        import oracle
+        g = 0  # KV head of query head 0
+        gk = [dks[c][:, g].cpu().numpy()[..., :d] for c in range(w.world)]
+        gv = [dvs[c][:, g].cpu().numpy()[..., :d] for c in range(w.world)]
+        pos = [oracle.positions(w.layout, w.seq_total, w.world, c) for c in range(w.world)]
+        res["dk"] = cmp(np.concatenate(gk, axis=1),
+                        np.concatenate([ref["dK"][:, g][:, p] for p in pos], axis=1))
+        res["dv"] = cmp(np.concatenate(gv, axis=1),
+                        np.concatenate([ref["dV"][:, g][:, p] for p in pos], axis=1))
+        res["dkdv_keys"] = int(w.seq_total)
     tol = (2e-2, 2e-3, 1e-2) if w.dtype == "bf16" else (1e-5, 1e-5, 1e-5)
     ok = all(res[k]["max_abs"] <= tol[0] and res[k]["mean_abs"] <= tol[1]
-             and res[k]["rel_fro"] <= tol[2] for k in ("o", "dq") if k in res)
+             and res[k]["rel_fro"] <= tol[2] for k in ("o", "dq", "dk", "dv") if k in res)
     res["pass"] = bool(ok and res["lse_max_abs"] <= 1e-3 and res["lse_inf_rows_match"])
     return res
 
@@ -480,7 +608,7 @@ def copy_probe(nbytes):
     print(json.dumps({"copy_probe_bytes": nbytes}), flush=True)
 
 
-def aux_bench(reps=50):
+def aux_bench(reps=50, only=None):
     """The HBM-bound helpers against the 8 TB/s roofline, at the llama_share and
     zigzag_fwdbwd shapes: the standalone LSE merge (rows x d fp32 partials) and the
     backward's delta = rowsum(dO * O) (bf16 inputs).  Algorithmic bytes per row:
@@ -506,7 +634,9 @@ def aux_bench(reps=50):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    for name, rows, d in (("llama_share", 1 * 16 * 8192, 128), ("zigzag_fwdbwd", 16 * 65536, 128)):
+    for name, (rows, d) in AUX_SHAPES.items():
+        if only is not None and name != only:
+            continue
         oa = torch.randn(rows, d, device=dev)
         op = torch.randn(rows, d, device=dev)
         la = torch.randn(rows, device=dev)
@@ -517,14 +647,15 @@ def aux_bench(reps=50):
         out["kernels"].append({"kernel": "lse_merge_kernel", "shape": f"{name}: {rows} rows x {d}",
                                "ms": round(ms, 4), "bytes": nbytes, "achieved": round(gbs, 1),
                                "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4)})
-    # reference: a plain device-to-device copy of 1 GiB (read + write)
-    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
-    dst = torch.empty_like(src)
-    ms = timed(lambda: dst.copy_(src))
-    gbs = 2 * src.numel() * 4 / (ms * 1e-3) / 1e9
-    out["copy_reference"] = {"bytes": 2 * src.numel() * 4, "ms": round(ms, 4),
-                             "achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    del src, dst
+    if only is None:
+        # reference: a plain device-to-device copy of 1 GiB (read + write)
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        ms = timed(lambda: dst.copy_(src))
+        gbs = 2 * src.numel() * 4 / (ms * 1e-3) / 1e9
+        out["copy_reference"] = {"bytes": 2 * src.numel() * 4, "ms": round(ms, 4),
+                                 "achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del src, dst
     B, H, L, D = 1, 16, 65536, 128
     o = torch.randn(B, H, L, D, device=dev).to(torch.bfloat16)
     do = torch.randn(B, H, L, D, device=dev).to(torch.bfloat16)
@@ -562,10 +693,108 @@ def time_fwd_steps(ra, prob, w, share, steps, ws, stream, reps):
     return [np.array([e[i].elapsed_time(e[i + 1]) for e in ev[1:]]) for i in range(n)]
 
 
+def _warm(fn, stream):
+    """Untimed warmup: at least 2 calls and about WARM_SECONDS of work."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    per = max(time.perf_counter() - t0, 1e-6)
+    for _ in range(min(5000, int(WARM_SECONDS / per))):
+        fn()
+    torch.cuda.synchronize()
+
+
+def other_config(name, reps, stream):
+    """One forward-only workload: ra_ring_fwd timed with HIP events over `reps` passes
+    after the default warmup, each live step timed on its own, and the outputs on
+    sampled rows and heads against the oracle (thread pool, fp64)."""
+    import numpy as np
+    import torch
+
+    from oracle.rows import attention_fwd_rows
+    from ring_context_parallelism_amd import ra, staging
+    from ring_context_parallelism_amd.workloads import WORKLOADS, generate
+    w = WORKLOADS[name]
+    print(f"[bench] config {name}: generating inputs", file=sys.stderr, flush=True)
+    arrays = generate(w)
+    dev = torch.device("cuda:0")
+    share = staging.stage(w, arrays, dev)
+    prob = share.prob
+    steps = step_flops(w, prob, ra)
+    L, D = w.chunk_len, w.head_dim_padded
+    out = torch.empty((w.batch, w.heads_q, L, D), dtype=staging.torch_dtype(w), device=dev)
+    lse = torch.empty((w.batch, w.heads_q, L), dtype=torch.float32, device=dev)
+    ws = torch.empty(ra.ra_ring_workspace_size(prob) // 4, dtype=torch.float32, device=dev)
+
+    def run():
+        ra.ra_ring_fwd(prob, w.rank, share.q, share.k_chunks, share.v_chunks, out, lse, ws,
+                       stream=stream)
+
+    _warm(run, stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    flop = sum(st["fwd_flop"] for st in steps)
+    peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
+    tf = flop / (float(np.mean(ms)) * 1e-3) / 1e12
+    step_ms = time_fwd_steps(ra, prob, w, share, steps, ws, stream, max(3, reps))
+    per_step = [dict(step=st["step"], chunk=st["chunk"],
+                     visible_pairs_per_head=st["visible_pairs_per_head"],
+                     fwd_ms=float(np.mean(sm)), fwd_ms_median=float(np.median(sm)),
+                     fwd_tflops=st["fwd_flop"] / (float(np.mean(sm)) * 1e-3) / 1e12,
+                     fwd_pct_peak=100.0 * st["fwd_flop"] / (float(np.mean(sm)) * 1e-3) / 1e12 / peak)
+                for st, sm in zip(steps, step_ms)]
+    # parity: sampled rows (tile edges + random) of sampled heads, or everything when small
+    run()
+    torch.cuda.synchronize()
+    small = L * w.heads_q * w.batch <= 4096
+    rng = np.random.default_rng(w.seed)
+    t_idx = np.arange(L) if small else np.unique(np.concatenate([
+        np.array([0, 1, 63, 64, 127, 128, 255, 256, L // 2, L - 129, L - 128, L - 2, L - 1]),
+        rng.choice(L, size=min(48, L), replace=False)]))
+    t_idx = t_idx[(t_idx >= 0) & (t_idx < L)]
+    heads = list(range(w.heads_q)) if small else sorted({0, w.heads_q - 1, *rng.choice(
+        w.heads_q, size=min(2, w.heads_q), replace=False).tolist()})
+    rows = share.rows[t_idx]
+    O, LSE = attention_fwd_rows(arrays["q"], arrays["k"], arrays["v"], rows, w.causal,
+                                heads=heads)
+    ti = torch.from_numpy(t_idx).to(dev)
+    got = out[:, heads][:, :, ti].float().cpu().numpy()[..., :w.head_dim]
+    lg = lse[:, heads][:, :, ti].cpu().numpy()
+    err = np.abs(got - O)
+    tol = (2e-2, 2e-3, 1e-2) if w.dtype == "bf16" else (1e-5, 1e-5, 1e-5)
+    par = {"rows": int(t_idx.size), "heads": heads, "max_abs": float(err.max()),
+           "mean_abs": float(err.mean()),
+           "rel_fro": float(np.linalg.norm(got - O) / np.linalg.norm(O)),
+           "lse_max_abs": float(np.abs(lg - LSE).max())}
+    par["pass"] = bool(par["max_abs"] <= tol[0] and par["mean_abs"] <= tol[1]
+                       and par["rel_fro"] <= tol[2] and par["lse_max_abs"] <= 1e-3)
+    rec = {"workload": name, "dtype": w.dtype, "batch": w.batch, "heads_q": w.heads_q,
+           "heads_kv": w.heads_kv, "head_dim": w.head_dim, "seq_total": w.seq_total,
+           "world": w.world, "layout": w.layout, "rank": w.rank, "causal": w.causal,
+           "passes": "fwd", "reps": reps, "fwd_ms": round(float(np.mean(ms)), 4),
+           "fwd_ms_median": round(float(np.median(ms)), 4), "flop": flop,
+           "fwd_tflops": round(tf, 3), "pct_peak": round(100.0 * tf / peak, 2),
+           "peak": peak, "per_step": per_step, "parity": par}
+    del share, arrays, out, lse, ws
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     args = parse()
     if args.aux:
-        aux_bench()
+        print("[bench] source hashes " + json.dumps({k: source_hash(f) for k, (_, f) in KERNELS.items()}),
+              file=sys.stderr, flush=True)
+        aux_bench(only=args.aux_shape)
         return
     if args.pmc_summary:
         print(pmc_summary(args.pmc_summary, args.workload))
@@ -716,12 +945,16 @@ def main():
         "wall_s": round(wall, 3),
     }
     if w.backward:
-        bwd_ms_total = float(np.mean([e[2].elapsed_time(e[-1]) for e in events]))
+        # the backward step: ra_bwd_prepare (delta, zero-fill), then every live step
+        bwd_ms_total = float(np.mean([e[1].elapsed_time(e[-1]) for e in events]))
+        kernels_ms = float(np.mean([e[2].elapsed_time(e[-1]) for e in events]))
         aux_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
         bwd_tflops = bwd_flop / (bwd_ms_total * 1e-3) / 1e12
         res["bwd"] = {"ms": round(bwd_ms_total, 4), "tflops": round(bwd_tflops, 3),
                       "pct_peak": round(100.0 * bwd_tflops / peak, 2), "flop": bwd_flop,
-                      "delta_and_zero_ms": round(aux_ms, 4)}
+                      "delta_and_zero_ms": round(aux_ms, 4),
+                      "step_kernels_pct_peak": round(
+                          100.0 * bwd_flop / (kernels_ms * 1e-3) / 1e12 / peak, 2)}
     # Dominant kernel: the one with the largest share of the step.  Algorithmic FLOP
     # per launch count only the contractions the method needs: forward 4d per
     # visible pair (QK^T, PV); dK/dV kernel 8d (S, dP, dV, dK); dQ kernel 2d (dQ --
@@ -753,7 +986,17 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
         res["cpu_baseline"], ref = cpu_baseline(w, arrays, args.cpu_seconds)
-        res["parity"] = sample_parity(w, ref, out, lse, dq if w.backward else None)
+        if w.backward:
+            res["parity"] = sample_parity(w, ref, out, lse, dq, dks, dvs)
+        else:
+            res["parity"] = sample_parity(w, ref, out, lse)
+    if not args.no_configs and args.workload == DEFAULT_WORKLOAD and args.dtype is None:
+        del share, arrays, out, lse, ws
+        if w.backward:
+            del delta, dq, dks, dvs
+        torch.cuda.empty_cache()
+        res["configs"] = [other_config(name, args.steps, stream)
+                          for name in OTHER_CONFIGS]
     print(json.dumps(res), flush=True)
 
 

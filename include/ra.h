@@ -98,7 +98,8 @@ typedef struct ra_problem_t {
   int64_t heads_kv;        /* Hkv >= 1, Hq % Hkv == 0 */
   int64_t head_dim;        /* true d (1..D); sets the default scale */
   int64_t head_dim_padded; /* D in {32, 64, 128} (storage) */
-  int64_t seq_total;       /* S; S % p == 0 (S % 2p == 0 for zigzag); S < 2^31 */
+  int64_t seq_total;       /* S; S % p == 0 (S % 2p == 0 for zigzag); S < 2^31;
+                              batch * heads_q * (S/p + 256) < 2^31 (one launch) */
   int32_t world;           /* p >= 1 */
   int32_t layout;          /* ra_layout_t */
   int32_t causal;          /* 0 or 1 */

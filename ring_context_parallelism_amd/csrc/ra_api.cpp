@@ -88,9 +88,12 @@ ra_status_t check_problem(const ra_problem_t* p) {
                   names[i]);
   if ((L + 256) * p->head_dim_padded * 4 >= (int64_t(1) << 32))
     return fail(RA_ERR_UNSUPPORTED, "chunk too long: one head's fp32 rows must span < 4 GiB");
+  // Every attention kernel launches at most 2 work-items per query row (or key) of a
+  // chunk rounded up to its tile, and one grid dimension holds fewer than 2^32.
   const int64_t rows = p->batch * p->heads_q;
-  if (rows * ((L + 127) / 128) >= (int64_t(1) << 31) || p->batch * p->heads_kv * L >= (int64_t(1) << 40))
-    return fail(RA_ERR_SHAPE, "problem too large for one launch");
+  if (rows * (L + 256) >= (int64_t(1) << 31))
+    return fail(RA_ERR_SHAPE,
+                "problem too large for one launch: batch * heads_q * (L + 256) must be < 2^31");
   return RA_OK;
 }
 

@@ -469,19 +469,22 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
 // Workgroup shape of the dQ kernel: 8 waves (256 query rows, each K/V tile serving
 // all of them) on dense sequences; 4 waves (128 rows, two workgroups per CU) with
-// packed documents, where fewer workgroups straddle a document boundary (6% faster
-// there, 2% slower on dense sequences).
-template <bool PACKED>
+// packed documents at head dim 128, where fewer workgroups straddle a document
+// boundary (7.7% faster there, 2% slower on dense sequences).  Other head dims keep
+// the 8-wave shape, on which they were measured.
+template <int D, bool PACKED>
 struct QCfg {
-  static constexpr int NT = PACKED ? 256 : 512;  // threads
-  static constexpr int BM = PACKED ? 128 : 256;  // query rows per workgroup
+  static constexpr int NW = (PACKED && D == 128) ? 4 : 8;
+  static constexpr int NT = 64 * NW;  // threads
+  static constexpr int BM = 32 * NW;  // query rows per workgroup
 };
 constexpr int kQBN = 32;        // keys per KV tile
 
 template <int D, bool PACKED>
-__global__ __launch_bounds__((QCfg<PACKED>::NT), (PACKED ? 2 : 1)) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int kQThreads = QCfg<PACKED>::NT;
-  constexpr int kQBM = QCfg<PACKED>::BM;
+__global__ __launch_bounds__((QCfg<D, PACKED>::NT), (QCfg<D, PACKED>::NW == 4 ? 2 : 1)) void bwd_dq_kernel(
+    BwdArgs a) {
+  constexpr int kQThreads = QCfg<D, PACKED>::NT;
+  constexpr int kQBM = QCfg<D, PACKED>::BM;
   constexpr int NKK = D / 32;  // 32-wide head-dim steps of the S^T and dP^T contractions
   constexpr int NDT = D / 16;  // 16-row head-dim tiles of dQ^T
   using PK = Pad<D>;
@@ -693,8 +696,8 @@ hipError_t launch(const BwdArgs& a, int which, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (which & 2) {
-    const int64_t nq = (int64_t)a.B * a.Hq * ((a.map.L + QCfg<PK>::BM - 1) / QCfg<PK>::BM);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, PK>), dim3((unsigned)nq), dim3(QCfg<PK>::NT), 0, s, a);
+    const int64_t nq = (int64_t)a.B * a.Hq * ((a.map.L + QCfg<D, PK>::BM - 1) / QCfg<D, PK>::BM);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, PK>), dim3((unsigned)nq), dim3(QCfg<D, PK>::NT), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -6,6 +6,12 @@ Python lists -> host pointer arrays) and turn a non-zero status into an
 exception.  All validation and every step of the computation happen in libra.so;
 there is no fallback: if the library is missing or fails to load, the first call
 raises.
+
+A call that returns normally has only ENQUEUED its kernels (the library's RA_OK): a
+device fault surfaces at the next synchronisation of the stream, which this binding
+does not perform.  With RA_SYNC_CHECK=1 in the environment, every call that launches
+kernels synchronises the device afterwards, so a fault is reported by the call that
+caused it (a debugging aid: it serialises the host with the GPU).
 """
 from __future__ import annotations
 
@@ -53,6 +59,8 @@ class Problem(ctypes.Structure):
         ("seg_bounds", ctypes.c_void_p),
     ]
 
+
+SYNC_CHECK = os.environ.get("RA_SYNC_CHECK", "0") not in ("", "0")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -105,6 +113,14 @@ def _status_name(st):
 def _check(st):
     if st != RA_OK:
         raise RaError(st, lib().ra_last_error().decode())
+
+
+def _launched(st):
+    """Status check of a call that enqueues kernels (plus the RA_SYNC_CHECK sync)."""
+    _check(st)
+    if SYNC_CHECK:
+        import torch
+        torch.cuda.synchronize()
 
 
 def _ptr(x):
@@ -160,12 +176,12 @@ def make_problem(*, batch, heads_q, heads_kv, head_dim, head_dim_padded, seq_tot
 # ------------------------------------------------------------------------ entry points
 
 def ra_block_attn_fwd(prob, q, q_chunk, k, v, kv_chunk, o, lse, mode, stream=None):
-    _check(lib().ra_block_attn_fwd(ctypes.byref(prob), _ptr(q), q_chunk, _ptr(k), _ptr(v),
+    _launched(lib().ra_block_attn_fwd(ctypes.byref(prob), _ptr(q), q_chunk, _ptr(k), _ptr(v),
                                    kv_chunk, _ptr(o), _ptr(lse), mode, _stream(stream)))
 
 
 def ra_lse_merge(rows, d, o_acc, lse_acc, o_part, lse_part, stream=None):
-    _check(lib().ra_lse_merge(rows, d, _ptr(o_acc), _ptr(lse_acc), _ptr(o_part),
+    _launched(lib().ra_lse_merge(rows, d, _ptr(o_acc), _ptr(lse_acc), _ptr(o_part),
                               _ptr(lse_part), _stream(stream)))
 
 
@@ -179,36 +195,36 @@ def ra_ring_fwd(prob, rank, q, k_chunks, v_chunks, out, lse, ws, ws_bytes=None, 
     ks, vs = _ptr_array(k_chunks), _ptr_array(v_chunks)
     if ws_bytes is None:
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().ra_ring_fwd(ctypes.byref(prob), rank, _ptr(q), ks, vs, _ptr(out), _ptr(lse),
+    _launched(lib().ra_ring_fwd(ctypes.byref(prob), rank, _ptr(q), ks, vs, _ptr(out), _ptr(lse),
                              _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def ra_bwd_delta(prob, out, dout, delta, stream=None):
-    _check(lib().ra_bwd_delta(ctypes.byref(prob), _ptr(out), _ptr(dout), _ptr(delta),
+    _launched(lib().ra_bwd_delta(ctypes.byref(prob), _ptr(out), _ptr(dout), _ptr(delta),
                               _stream(stream)))
 
 
 def ra_bwd_prepare(prob, out, dout, delta, dq, dk_chunks, dv_chunks, stream=None):
-    _check(lib().ra_bwd_prepare(ctypes.byref(prob), _ptr(out), _ptr(dout), _ptr(delta), _ptr(dq),
+    _launched(lib().ra_bwd_prepare(ctypes.byref(prob), _ptr(out), _ptr(dout), _ptr(delta), _ptr(dq),
                                 _ptr_array(dk_chunks), _ptr_array(dv_chunks), _stream(stream)))
 
 
 def ra_block_attn_bwd(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dq, dk, dv,
                       stream=None):
-    _check(lib().ra_block_attn_bwd(ctypes.byref(prob), _ptr(q), q_chunk, _ptr(k), _ptr(v),
+    _launched(lib().ra_block_attn_bwd(ctypes.byref(prob), _ptr(q), q_chunk, _ptr(k), _ptr(v),
                                    kv_chunk, _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq),
                                    _ptr(dk), _ptr(dv), _stream(stream)))
 
 
 def ra_block_attn_bwd_dkdv(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dk, dv,
                            stream=None):
-    _check(lib().ra_block_attn_bwd_dkdv(ctypes.byref(prob), _ptr(q), q_chunk, _ptr(k), _ptr(v),
+    _launched(lib().ra_block_attn_bwd_dkdv(ctypes.byref(prob), _ptr(q), q_chunk, _ptr(k), _ptr(v),
                                         kv_chunk, _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dk),
                                         _ptr(dv), _stream(stream)))
 
 
 def ra_block_attn_bwd_dq(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dq, stream=None):
-    _check(lib().ra_block_attn_bwd_dq(ctypes.byref(prob), _ptr(q), q_chunk, _ptr(k), _ptr(v),
+    _launched(lib().ra_block_attn_bwd_dq(ctypes.byref(prob), _ptr(q), q_chunk, _ptr(k), _ptr(v),
                                       kv_chunk, _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq),
                                       _stream(stream)))
 
@@ -223,7 +239,7 @@ def ra_ring_bwd(prob, rank, q, k_chunks, v_chunks, out, dout, lse, dq, dk_chunks
                 ws, ws_bytes=None, stream=None):
     if ws_bytes is None:
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().ra_ring_bwd(ctypes.byref(prob), rank, _ptr(q), _ptr_array(k_chunks),
+    _launched(lib().ra_ring_bwd(ctypes.byref(prob), rank, _ptr(q), _ptr_array(k_chunks),
                              _ptr_array(v_chunks), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
                              _ptr_array(dk_chunks), _ptr_array(dv_chunks), _ptr(ws), ws_bytes,
                              _stream(stream)))

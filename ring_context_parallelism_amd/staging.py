@@ -67,30 +67,41 @@ def stage(w: Workload, arrays: dict, device="cuda", rank: int | None = None) -> 
     return Share(prob, q, ks, vs, do, rows, bounds)
 
 
-def ring_forward(share: Share, w: Workload, rank: int | None = None, stream=None):
-    """Runs ra_ring_fwd on a staged share; returns (out [B, Hq, L, D], lse fp32)."""
+def _empty(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+def ring_forward(share: Share, w: Workload, rank: int | None = None, stream=None, alloc=None):
+    """Runs ra_ring_fwd on a staged share; returns (out [B, Hq, L, D], lse fp32).
+
+    alloc(shape, dtype, device) -> tensor allocates the outputs and the workspace
+    (default: torch.empty)."""
     rank = w.rank if rank is None else rank
+    alloc = alloc or _empty
     L, D = w.chunk_len, w.head_dim_padded
     dev = share.q.device
-    out = torch.empty((w.batch, w.heads_q, L, D), dtype=torch_dtype(w), device=dev)
-    lse = torch.empty((w.batch, w.heads_q, L), dtype=torch.float32, device=dev)
-    ws = torch.empty(ra.ra_ring_workspace_size(share.prob) // 4, dtype=torch.float32, device=dev)
+    out = alloc((w.batch, w.heads_q, L, D), torch_dtype(w), dev)
+    lse = alloc((w.batch, w.heads_q, L), torch.float32, dev)
+    ws = alloc((ra.ra_ring_workspace_size(share.prob) // 4,), torch.float32, dev)
     ra.ra_ring_fwd(share.prob, rank, share.q, share.k_chunks, share.v_chunks, out, lse, ws,
                    stream=stream)
     return out, lse
 
 
-def ring_backward(share: Share, w: Workload, out, lse, rank: int | None = None, stream=None):
-    """Runs ra_ring_bwd; returns (dq, dk_chunks, dv_chunks), fp32 [B, H, L, D]."""
+def ring_backward(share: Share, w: Workload, out, lse, rank: int | None = None, stream=None,
+                  alloc=None):
+    """Runs ra_ring_bwd; returns (dq, dk_chunks, dv_chunks), fp32 [B, H, L, D].
+
+    alloc as in ring_forward (gradients and workspace)."""
     rank = w.rank if rank is None else rank
+    alloc = alloc or _empty
     L, D = w.chunk_len, w.head_dim_padded
     dev = share.q.device
-    dq = torch.empty((w.batch, w.heads_q, L, D), dtype=torch.float32, device=dev)
-    dks = [torch.empty((w.batch, w.heads_kv, L, D), dtype=torch.float32, device=dev)
-           for _ in range(w.world)]
-    dvs = [torch.empty_like(dks[0]) for _ in range(w.world)]
-    ws = torch.empty(ra.ra_ring_bwd_workspace_size(share.prob) // 4, dtype=torch.float32,
-                     device=dev)
+    f32 = torch.float32
+    dq = alloc((w.batch, w.heads_q, L, D), f32, dev)
+    dks = [alloc((w.batch, w.heads_kv, L, D), f32, dev) for _ in range(w.world)]
+    dvs = [alloc((w.batch, w.heads_kv, L, D), f32, dev) for _ in range(w.world)]
+    ws = alloc((ra.ra_ring_bwd_workspace_size(share.prob) // 4,), f32, dev)
     ra.ra_ring_bwd(share.prob, rank, share.q, share.k_chunks, share.v_chunks, out, share.do,
                    lse, dq, dks, dvs, ws, stream=stream)
     return dq, dks, dvs

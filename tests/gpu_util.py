@@ -55,6 +55,27 @@ def assert_lse(got, ref, what):
         assert err <= LSE_TOL, f"{what}: LSE max abs error {err}"
 
 
+class Guarded:
+    """Allocator of output buffers with a NaN guard tail (SURVEY's race-detection
+    canaries): every buffer starts as NaN, so an element a kernel fails to write
+    stays NaN and fails the comparison, and `check()` asserts that no write went
+    past the end of any buffer."""
+
+    def __init__(self, guard=4096):
+        self.guard = guard
+        self.tails = []
+
+    def __call__(self, shape, dtype, device):
+        n = int(np.prod(shape))
+        buf = torch.full((n + self.guard,), float("nan"), dtype=dtype, device=device)
+        self.tails.append(buf[n:])
+        return buf[:n].view(shape)
+
+    def check(self, what=""):
+        for i, t in enumerate(self.tails):
+            assert torch.isnan(t).all().item(), f"{what}: write past the end of buffer {i}"
+
+
 def sample_rows(L, n_random=48, seed=0):
     """Local row indices: tile edges, both ends, the middle, plus random rows."""
     rng = np.random.default_rng(seed)

@@ -134,6 +134,8 @@ FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced on thes
     (dict(kv_stride=(0, 0, 1 << 24)), ra.RA_ERR_UNSUPPORTED),  # a head's rows span > 4 GiB
     (dict(o_stride=(0, 0, 1 << 24)), ra.RA_ERR_UNSUPPORTED),
     (dict(scale=-1.0), ra.RA_ERR_SHAPE),
+    # batch * heads_q * (L + 256) >= 2^31: more work-items than one grid dimension holds
+    (dict(batch=1 << 12, heads_q=1 << 10, heads_kv=1 << 10, seq_total=4096), ra.RA_ERR_SHAPE),
     (dict(seg_bounds=FAKE, seg_count=1), ra.RA_ERR_SHAPE),
     (dict(seg_bounds=FAKE, seg_count=0), ra.RA_ERR_SHAPE),
     (dict(seg_bounds=FAKE + 2, seg_count=4), ra.RA_ERR_SHAPE),

@@ -5,9 +5,9 @@
   dK, dV of every KV chunk -- element by element;
 * ra_block_attn_bwd accumulates (+=) and a step with no visible pair is a no-op;
 * ra_bwd_delta against the oracle's rowsum(dO * O);
-* the forward+backward zigzag workload at full size: dQ on sampled rows and heads
-  the oracle computes one by one, plus two identities that hold at any size,
-  sum_j dV_j = sum_i dO_i and sum_j dK_j = 0 (per KV head).
+* the forward+backward zigzag workload at full size: dQ of every row and dK, dV of
+  every key for two heads, element by element, plus two identities that hold at
+  any size over all heads, sum_j dV_j = sum_i dO_i and sum_j dK_j = 0 (per KV head).
 """
 import numpy as np
 import pytest
@@ -16,7 +16,7 @@ import torch
 import oracle
 from ring_context_parallelism_amd import ra, staging
 from ring_context_parallelism_amd.workloads import WORKLOADS, Workload, generate
-from tests.gpu_util import assert_close, need_gpu, sample_heads, sample_rows, say, stats
+from tests.gpu_util import Guarded, assert_close, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -54,9 +54,11 @@ def test_ring_bwd_every_rank(w):
     for r in range(w.world):
         say(f"ring_bwd {_ids(w)} rank {r}")
         share = staging.stage(w, arrays, dev, rank=r)
-        out, lse = staging.ring_forward(share, w, rank=r)
-        dq, dks, dvs = staging.ring_backward(share, w, out, lse, rank=r)
+        guard = Guarded()
+        out, lse = staging.ring_forward(share, w, rank=r, alloc=guard)
+        dq, dks, dvs = staging.ring_backward(share, w, out, lse, rank=r, alloc=guard)
         torch.cuda.synchronize()
+        guard.check(f"ring fwd+bwd rank {r}")
         rows = oracle.positions(w.layout, w.seq_total, w.world, r)
         dQ, dK, dV = oracle.attention_bwd(arrays["q"], arrays["k"], arrays["v"],
                                           arrays["do"][:, :, rows], rows, w.causal)
@@ -142,33 +144,32 @@ def test_bwd_prepare_delta_and_zero_fill():
         assert torch.isnan(t[n:]).all()
 
 
-def test_full_size_backward_sampled_and_identities():
+@pytest.mark.timeout(900)
+def test_full_size_backward_two_heads_elementwise():
+    """The zig-zag forward+backward share at full size (16 heads x d 128, S 131072, p 2,
+    rank 0), in the launch configuration the benchmark times.  For the first and the
+    last head: dQ of all 65,536 rank-0 rows and dK, dV of every key of both KV chunks,
+    element by element against the oracle (its rows spread over a thread pool); dK and
+    dV accumulate bf16 P and dS over up to 65,536 query rows per key.  Over all heads:
+    sum_j dV_j = sum_i dO_i and sum_j dK_j = 0 per KV head, and NaN guard tails past
+    every output buffer stay untouched."""
+    from oracle.rows import attention_bwd_rows, default_workers
     dev = need_gpu()
     w = WORKLOADS["zigzag_fwdbwd"]
     say("full-size backward: generating inputs")
     arrays = generate(w)
     share = staging.stage(w, arrays, dev)
     say("full-size backward: ra_ring_fwd + ra_ring_bwd")
-    out, lse = staging.ring_forward(share, w)
-    dq, dks, dvs = staging.ring_backward(share, w, out, lse)
+    guard = Guarded()
+    out, lse = staging.ring_forward(share, w, alloc=guard)
+    dq, dks, dvs = staging.ring_backward(share, w, out, lse, alloc=guard)
     torch.cuda.synchronize()
+    guard.check("full-size backward")
     assert torch.isfinite(dq).all()
-    L, d = w.chunk_len, w.head_dim
-    t_idx = sample_rows(L, n_random=24, seed=7)
-    heads = sample_heads(w.heads_q, seed=7)
-    rows_all = oracle.positions(w.layout, w.seq_total, w.world, w.rank)
-    rows = rows_all[t_idx]
-    say(f"full-size backward: oracle dQ on {len(t_idx)} rows x {len(heads)} heads")
-    dO = arrays["do"][:, heads][:, :, rows]
-    dQ, _, _ = oracle.attention_bwd(arrays["q"], arrays["k"], arrays["v"], dO, rows, w.causal,
-                                    heads=heads)
-    got = dq[:, heads][:, :, torch.from_numpy(t_idx).to(dev)].cpu().numpy()
-    s = assert_close(got[..., :d], dQ, "bf16", "dQ sampled")
-    say(f"full-size backward: dQ {s}")
+    d, group = w.head_dim, w.heads_q // w.heads_kv
     # identities over the whole share: sum_j dV_j = sum_i dO_i and sum_j dK_j = 0
-    g = w.heads_q // w.heads_kv
-    do_sum = share.do.double().sum(dim=2)                        # [B, Hq, D]
-    do_sum = do_sum.view(w.batch, w.heads_kv, g, -1).sum(dim=2)  # per KV head
+    do_sum = share.do.double().sum(dim=2)                            # [B, Hq, D]
+    do_sum = do_sum.view(w.batch, w.heads_kv, group, -1).sum(dim=2)  # per KV head
     dv_sum = sum(x.double().sum(dim=2) for x in dvs)
     dk_sum = sum(x.double().sum(dim=2) for x in dks)
     dk_fro = torch.sqrt(sum((x.double() ** 2).sum(dim=(2, 3)) for x in dks))
@@ -177,6 +178,23 @@ def test_full_size_backward_sampled_and_identities():
     say(f"full-size backward: |sum dV - sum dO|/|sum dO| = {rel_v:.2e}, "
         f"|sum dK|/|dK|_F = {rel_k:.2e}")
     assert rel_v < 1e-2 and rel_k < 2e-2
+    heads = [0, w.heads_q - 1]
+    rows = oracle.positions(w.layout, w.seq_total, w.world, w.rank)
+    say(f"full-size backward: oracle on all {rows.size} rows of heads {heads}, "
+        f"{default_workers()} threads")
+    dQ, dK, dV = attention_bwd_rows(arrays["q"], arrays["k"], arrays["v"],
+                                    arrays["do"][:, heads][:, :, rows], rows, w.causal,
+                                    heads=heads)
+    s = assert_close(_np(dq[:, heads])[..., :d], dQ, "bf16", "dQ")
+    say(f"full-size backward: dQ {s}")
+    for g in sorted({h // group for h in heads}):
+        for c in range(w.world):
+            pos = oracle.positions(w.layout, w.seq_total, w.world, c)
+            sk = assert_close(_np(dks[c][:, g])[..., :d], dK[:, g][:, pos], "bf16",
+                              f"dK KV head {g} chunk {c}")
+            sv = assert_close(_np(dvs[c][:, g])[..., :d], dV[:, g][:, pos], "bf16",
+                              f"dV KV head {g} chunk {c}")
+            say(f"full-size backward: KV head {g} chunk {c}: dK {sk}  dV {sv}")
 
 
 def test_split_entry_points_match_combined():

@@ -12,7 +12,7 @@ import torch
 import oracle
 from ring_context_parallelism_amd import staging
 from ring_context_parallelism_amd.workloads import Workload, generate
-from tests.gpu_util import assert_close, assert_lse, need_gpu, say
+from tests.gpu_util import Guarded, assert_close, assert_lse, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -63,8 +63,10 @@ def _check_share(w, arrays, bounds, dev):
     for r in range(w.world):
         say(f"edge {_ids(w)} rank {r}")
         share = staging.stage(w, arrays, dev, rank=r)
-        out, lse = staging.ring_forward(share, w, rank=r)
+        guard = Guarded()
+        out, lse = staging.ring_forward(share, w, rank=r, alloc=guard)
         torch.cuda.synchronize()
+        guard.check(f"edge forward rank {r}")
         rows = oracle.positions(w.layout, w.seq_total, w.world, r)
         O, LSE = oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal,
                                       bounds=bounds)
@@ -74,8 +76,9 @@ def _check_share(w, arrays, bounds, dev):
         assert_lse(_np(lse), LSE, f"LSE rank {r}")
         if not w.backward:
             continue
-        dq, dks, dvs = staging.ring_backward(share, w, out, lse, rank=r)
+        dq, dks, dvs = staging.ring_backward(share, w, out, lse, rank=r, alloc=guard)
         torch.cuda.synchronize()
+        guard.check(f"edge backward rank {r}")
         dQ, dK, dV = oracle.attention_bwd(arrays["q"], arrays["k"], arrays["v"],
                                           arrays["do"][:, :, rows], rows, w.causal, bounds=bounds)
         assert_close(_np(dq)[..., :d], dQ, "bf16", f"dQ rank {r}")

@@ -16,7 +16,8 @@ import torch
 import oracle
 from ring_context_parallelism_amd import ra, staging
 from ring_context_parallelism_amd.workloads import WORKLOADS, Workload, generate, round_bf16
-from tests.gpu_util import assert_close, assert_lse, need_gpu, sample_heads, sample_rows, say
+from tests.gpu_util import (Guarded, assert_close, assert_lse, need_gpu, sample_heads,
+                            sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -58,8 +59,10 @@ def test_ring_fwd_every_rank(w):
     for r in range(w.world):
         say(f"ring_fwd {_ids(w)} rank {r}")
         share = staging.stage(w, arrays, dev, rank=r)
-        out, lse = staging.ring_forward(share, w, rank=r)
+        guard = Guarded()
+        out, lse = staging.ring_forward(share, w, rank=r, alloc=guard)
         torch.cuda.synchronize()
+        guard.check(f"ring_fwd rank {r}")
         rows = oracle.positions(w.layout, w.seq_total, w.world, r)
         assert np.array_equal(rows, share.rows)
         O, LSE = oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal)
@@ -103,8 +106,10 @@ def test_ring_fwd_moving_max(w):
     for r in range(w.world):
         say(f"moving max {_ids(w)} rank {r}")
         share = staging.stage(w, arrays, dev, rank=r)
-        out, lse = staging.ring_forward(share, w, rank=r)
+        guard = Guarded()
+        out, lse = staging.ring_forward(share, w, rank=r, alloc=guard)
         torch.cuda.synchronize()
+        guard.check(f"moving max rank {r}")
         rows = oracle.positions(w.layout, w.seq_total, w.world, r)
         O, LSE = oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal)
         assert LSE.max() - LSE.min() > 15.0, "the inputs must move the row maxima"
@@ -128,13 +133,15 @@ def test_block_fwd_partials_and_merge(w):
         for s, ck in enumerate(oracle.ring_schedule(cq, w.world)):
             say(f"block_fwd {_ids(w)} q_chunk {cq} kv_chunk {ck}")
             kpos = oracle.positions(w.layout, w.seq_total, w.world, ck)
-            o = torch.empty((w.batch, w.heads_q, L, D), dtype=torch.float32, device=dev)
-            lse = torch.empty((w.batch, w.heads_q, L), dtype=torch.float32, device=dev)
+            guard = Guarded()
+            o = guard((w.batch, w.heads_q, L, D), torch.float32, dev)
+            lse = guard((w.batch, w.heads_q, L), torch.float32, dev)
             ra.ra_block_attn_fwd(share.prob, share.q, cq, share.k_chunks[ck], share.v_chunks[ck],
                                  ck, o, lse, ra.RA_WRITE)
             ra.ra_block_attn_fwd(share.prob, share.q, cq, share.k_chunks[ck], share.v_chunks[ck],
                                  ck, o_acc, l_acc, ra.RA_MERGE)
             torch.cuda.synchronize()
+            guard.check(f"partial ({cq},{ck})")
             Op, Lp = oracle.attention_partial(arrays["q"][:, :, qpos], arrays["k"][:, :, kpos],
                                               arrays["v"][:, :, kpos], qpos, kpos, w.causal,
                                               scale, w.heads_q, w.heads_kv)
@@ -197,8 +204,10 @@ def test_full_size_forward_sampled(w):
     arrays = generate(w)
     share = staging.stage(w, arrays, dev)
     say(f"full-size forward {w.name} {w.dtype}: ra_ring_fwd")
-    out, lse = staging.ring_forward(share, w)
+    guard = Guarded()
+    out, lse = staging.ring_forward(share, w, alloc=guard)
     torch.cuda.synchronize()
+    guard.check(f"full-size forward {w.name}")
     L, d = w.chunk_len, w.head_dim
     full = w.name == "tiny_fp32"
     t_idx = np.arange(L) if full else sample_rows(L, seed=w.seed)

@@ -22,7 +22,8 @@ import torch
 import oracle
 from ring_context_parallelism_amd import ra, staging
 from ring_context_parallelism_amd.workloads import WORKLOADS, Workload, document_bounds, generate
-from tests.gpu_util import assert_close, assert_lse, need_gpu, sample_heads, sample_rows, say
+from tests.gpu_util import (Guarded, assert_close, assert_lse, need_gpu, sample_heads,
+                            sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -99,8 +100,10 @@ def test_packed_ring_fwd_every_rank(case):
     for r in range(w.world):
         say(f"packed ring_fwd {_ids(case)} rank {r}")
         share = staging.stage(w, arrays, dev, rank=r)
-        out, lse = staging.ring_forward(share, w, rank=r)
+        guard = Guarded()
+        out, lse = staging.ring_forward(share, w, rank=r, alloc=guard)
         torch.cuda.synchronize()
+        guard.check(f"packed ring_fwd rank {r}")
         rows = oracle.positions(w.layout, w.seq_total, w.world, r)
         O, LSE = oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal,
                                       bounds=bounds)
@@ -129,13 +132,15 @@ def test_packed_block_fwd_partials_and_merge(case):
         for ck in oracle.ring_schedule(cq, w.world):
             say(f"packed block_fwd {_ids(case)} q_chunk {cq} kv_chunk {ck}")
             kpos = oracle.positions(w.layout, w.seq_total, w.world, ck)
-            o = torch.empty((w.batch, w.heads_q, L, D), dtype=torch.float32, device=dev)
-            lse = torch.empty((w.batch, w.heads_q, L), dtype=torch.float32, device=dev)
+            guard = Guarded()
+            o = guard((w.batch, w.heads_q, L, D), torch.float32, dev)
+            lse = guard((w.batch, w.heads_q, L), torch.float32, dev)
             ra.ra_block_attn_fwd(share.prob, share.q, cq, share.k_chunks[ck], share.v_chunks[ck],
                                  ck, o, lse, ra.RA_WRITE)
             ra.ra_block_attn_fwd(share.prob, share.q, cq, share.k_chunks[ck], share.v_chunks[ck],
                                  ck, o_acc, l_acc, ra.RA_MERGE)
             torch.cuda.synchronize()
+            guard.check(f"packed partial ({cq},{ck})")
             Op, Lp = oracle.attention_partial(arrays["q"][:, :, qpos], arrays["k"][:, :, kpos],
                                               arrays["v"][:, :, kpos], qpos, kpos, w.causal,
                                               scale, w.heads_q, w.heads_kv, bounds=bounds,
@@ -159,9 +164,11 @@ def test_packed_ring_bwd_every_rank(case):
     for r in range(w.world):
         say(f"packed ring_bwd {_ids(case)} rank {r}")
         share = staging.stage(w, arrays, dev, rank=r)
-        out, lse = staging.ring_forward(share, w, rank=r)
-        dq, dks, dvs = staging.ring_backward(share, w, out, lse, rank=r)
+        guard = Guarded()
+        out, lse = staging.ring_forward(share, w, rank=r, alloc=guard)
+        dq, dks, dvs = staging.ring_backward(share, w, out, lse, rank=r, alloc=guard)
         torch.cuda.synchronize()
+        guard.check(f"packed ring fwd+bwd rank {r}")
         rows = oracle.positions(w.layout, w.seq_total, w.world, r)
         dQ, dK, dV = oracle.attention_bwd(arrays["q"], arrays["k"], arrays["v"],
                                           arrays["do"][:, :, rows], rows, w.causal, bounds=bounds)
@@ -180,7 +187,12 @@ def test_packed_ring_bwd_every_rank(case):
         say(f"  dQ {s}")
 
 
+@pytest.mark.timeout(600)
 def test_packed_full_size_sampled_and_identities():
+    """The packed share at full size: O and LSE on sampled rows (tile and document
+    edges), dQ of every row and dK, dV of every key of both chunks for head 0 element
+    by element, identities over all heads, and NaN guard tails."""
+    from oracle.rows import attention_bwd_rows
     dev = need_gpu()
     w = WORKLOADS["packed_fwdbwd"]
     say("packed full size: generating inputs")
@@ -188,9 +200,11 @@ def test_packed_full_size_sampled_and_identities():
     bounds = _bounds_list(arrays)
     share = staging.stage(w, arrays, dev)
     say("packed full size: ra_ring_fwd + ra_ring_bwd")
-    out, lse = staging.ring_forward(share, w)
-    dq, dks, dvs = staging.ring_backward(share, w, out, lse)
+    guard = Guarded()
+    out, lse = staging.ring_forward(share, w, alloc=guard)
+    dq, dks, dvs = staging.ring_backward(share, w, out, lse, alloc=guard)
     torch.cuda.synchronize()
+    guard.check("packed full size")
     L, d = w.chunk_len, w.head_dim
     rows_all = oracle.positions(w.layout, w.seq_total, w.world, w.rank)
     # sampled rows: tile edges and random rows, plus rows at every document edge
@@ -206,12 +220,20 @@ def test_packed_full_size_sampled_and_identities():
     got = out[:, heads][:, :, ti].float().cpu().numpy()
     assert_close(got[..., :d], O, "bf16", "O sampled")
     assert_lse(lse[:, heads][:, :, ti].cpu().numpy(), LSE, "LSE sampled")
-    dO = arrays["do"][:, heads][:, :, rows]
-    dQ, _, _ = oracle.attention_bwd(arrays["q"], arrays["k"], arrays["v"], dO, rows, w.causal,
-                                    heads=heads, bounds=bounds)
-    gq = dq[:, heads][:, :, ti].cpu().numpy()
-    s = assert_close(gq[..., :d], dQ, "bf16", "dQ sampled")
+    say("packed full size: oracle backward on every row of head 0")
+    dQ, dK, dV = attention_bwd_rows(arrays["q"], arrays["k"], arrays["v"],
+                                    arrays["do"][:, :1][:, :, rows_all], rows_all, w.causal,
+                                    heads=[0], bounds=bounds)
+    s = assert_close(dq[:, :1].cpu().numpy()[..., :d], dQ, "bf16", "dQ head 0")
     say(f"packed full size: dQ {s}")
+    g0 = 0  # KV head of query head 0
+    for c in range(w.world):
+        pos = oracle.positions(w.layout, w.seq_total, w.world, c)
+        sk = assert_close(dks[c][:, g0].cpu().numpy()[..., :d], dK[:, g0][:, pos], "bf16",
+                          f"dK chunk {c}")
+        sv = assert_close(dvs[c][:, g0].cpu().numpy()[..., :d], dV[:, g0][:, pos], "bf16",
+                          f"dV chunk {c}")
+        say(f"packed full size: chunk {c}: dK {sk}  dV {sv}")
     # identities over the whole share
     live = torch.from_numpy(rows_all < bounds[0][-1]).to(dev)
     g = w.heads_q // w.heads_kv
