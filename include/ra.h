@@ -230,6 +230,23 @@ ra_status_t ra_ring_bwd(const ra_problem_t* prob, int32_t rank, const void* q,
                         float* const* dk_chunks, float* const* dv_chunks, void* ws,
                         size_t ws_bytes, hipStream_t stream);
 
+/*
+ * ra_ring_bwd without a workspace argument, for callers that cannot allocate (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the fp32 delta workspace lives in a static device array of 16 MiB, so
+ * batch * heads_q * L <= 4,194,304 (RA_ERR_WORKSPACE otherwise, before anything is
+ * enqueued).  The call allocates nothing; each GPU holds its own copy of the array
+ * until the process ends, and its device address is looked up on the first call on
+ * that device.  Every call on one GPU shares that GPU's array: two calls that
+ * overlap on one GPU (on different streams, or from different threads) race and
+ * give unspecified gradients.  Other arguments, results and errors as ra_ring_bwd.
+ */
+ra_status_t ra_ring_bwd_noalloc(const ra_problem_t* prob, int32_t rank, const void* q,
+                                const void* const* k_chunks, const void* const* v_chunks,
+                                const void* out, const void* dout, const float* lse, float* dq,
+                                float* const* dk_chunks, float* const* dv_chunks,
+                                hipStream_t stream);
+
 /* Host only.  host_out[t] = pos(chunk, t) for t in [0, L).  No device access. */
 ra_status_t ra_positions(const ra_problem_t* prob, int32_t chunk, int64_t* host_out);
 

@@ -15,7 +15,7 @@ LIB = os.path.join(HERE, "libra.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["ra_api.cpp", "ra_fwd.hip", "ra_bwd.hip", "ra_misc.hip"]
+SOURCES = ["ra_api.cpp", "ra_fwd.hip", "ra_bwd.hip", "ra_misc.hip", "ra_noalloc.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

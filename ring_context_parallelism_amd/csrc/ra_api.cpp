@@ -533,4 +533,24 @@ ra_status_t ra_ring_bwd(const ra_problem_t* prob, int32_t rank, const void* q,
   return ok();
 }
 
+ra_status_t ra_ring_bwd_noalloc(const ra_problem_t* prob, int32_t rank, const void* q,
+                                const void* const* k_chunks, const void* const* v_chunks,
+                                const void* out, const void* dout, const float* lse, float* dq,
+                                float* const* dk_chunks, float* const* dv_chunks,
+                                hipStream_t stream) {
+  RA_TRY(check_problem(prob));
+  size_t need = 0;
+  RA_TRY(ra_ring_bwd_workspace_size(prob, &need));
+  if (need > ra::kStaticScratchBytes)
+    return fail(RA_ERR_WORKSPACE,
+                "needs %zu bytes of workspace; the static scratch holds %zu "
+                "(batch * heads_q * L <= %zu)",
+                need, ra::kStaticScratchBytes, ra::kStaticScratchBytes / sizeof(float));
+  void* ws = nullptr;
+  const hipError_t e = ra::static_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "ra_ring_bwd_noalloc: static scratch address");
+  return ra_ring_bwd(prob, rank, q, k_chunks, v_chunks, out, dout, lse, dq, dk_chunks,
+                     dv_chunks, ws, ra::kStaticScratchBytes, stream);
+}
+
 }  // extern "C"

@@ -204,4 +204,9 @@ hipError_t launch_bwd_delta(int dtype, int32_t B, int32_t H, int32_t L, int32_t 
                             int64_t st, float* delta, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s);
 
+// Static device scratch of ra_ring_bwd_noalloc (ra_noalloc.hip): its size, and the
+// device address of the current device's copy (looked up once per device).
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+hipError_t static_scratch(void** ptr);
+
 }  // namespace ra

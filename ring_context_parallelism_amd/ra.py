@@ -35,7 +35,7 @@ DTYPE_IDS = {"f32": RA_F32, "bf16": RA_BF16}
 EXPORTS = [
     "ra_block_attn_fwd", "ra_lse_merge", "ra_ring_workspace_size", "ra_ring_fwd",
     "ra_bwd_delta", "ra_bwd_prepare", "ra_block_attn_bwd", "ra_block_attn_bwd_dkdv", "ra_block_attn_bwd_dq",
-    "ra_ring_bwd_workspace_size", "ra_ring_bwd",
+    "ra_ring_bwd_workspace_size", "ra_ring_bwd", "ra_ring_bwd_noalloc",
     "ra_positions", "ra_visible_pairs", "ra_visible_pairs_packed", "ra_status_str",
     "ra_last_error",
 ]
@@ -88,6 +88,7 @@ def lib():
             "ra_block_attn_bwd_dq": [_PROB, _P, _I32, _P, _P, _I32, _P, _P, _P, _P, _P],
             "ra_ring_bwd_workspace_size": [_PROB, ctypes.POINTER(_SZ)],
             "ra_ring_bwd": [_PROB, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+            "ra_ring_bwd_noalloc": [_PROB, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
             "ra_positions": [_PROB, _I32, ctypes.POINTER(_I64)],
             "ra_visible_pairs": [_PROB, _I32, _I32, ctypes.POINTER(_I64)],
             "ra_visible_pairs_packed": [_PROB, _I32, _I32, ctypes.POINTER(_I32),
@@ -243,6 +244,14 @@ def ra_ring_bwd(prob, rank, q, k_chunks, v_chunks, out, dout, lse, dq, dk_chunks
                              _ptr_array(v_chunks), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
                              _ptr_array(dk_chunks), _ptr_array(dv_chunks), _ptr(ws), ws_bytes,
                              _stream(stream)))
+
+
+def ra_ring_bwd_noalloc(prob, rank, q, k_chunks, v_chunks, out, dout, lse, dq, dk_chunks,
+                        dv_chunks, stream=None):
+    _launched(lib().ra_ring_bwd_noalloc(ctypes.byref(prob), rank, _ptr(q), _ptr_array(k_chunks),
+                                        _ptr_array(v_chunks), _ptr(out), _ptr(dout), _ptr(lse),
+                                        _ptr(dq), _ptr_array(dk_chunks), _ptr_array(dv_chunks),
+                                        _stream(stream)))
 
 
 def ra_positions(prob, chunk) -> np.ndarray:

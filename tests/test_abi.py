@@ -187,3 +187,16 @@ def test_call_validation():
 def test_status_strings():
     assert ra.ra_status_str(ra.RA_OK) == "RA_OK"
     assert ra.ra_status_str(ra.RA_ERR_WORKSPACE) == "RA_ERR_WORKSPACE"
+
+
+def test_noalloc_refuses_a_workspace_beyond_the_static_array_before_any_launch():
+    # batch * heads_q * L = 64 * 131072 rows of fp32 delta > the 16 MiB static array
+    p = _prob(heads_q=64, heads_kv=8, head_dim=128, head_dim_padded=128, seq_total=131072,
+              world=1)
+    ks = [FAKE]
+    assert _status_of(ra.ra_ring_bwd_noalloc, p, 0, FAKE, ks, ks, FAKE, FAKE, FAKE, FAKE, ks,
+                      ks, 0) == ra.RA_ERR_WORKSPACE
+    assert "static scratch" in ra.ra_last_error()
+    # the problem checks come first
+    assert _status_of(ra.ra_ring_bwd_noalloc, _prob(world=0), 0, FAKE, ks, ks, FAKE, FAKE, FAKE,
+                      FAKE, ks, ks, 0) == ra.RA_ERR_SHAPE
