@@ -30,12 +30,19 @@ if ROOT not in sys.path:
 BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 F32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix
 # Vector ALU: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz = 39.3 T lane-operations/s for
-# full-rate fp32 instructions without the packed forms (exp and add have none).
+# full-rate fp32 instructions (a wave64 instruction occupies a SIMD for 4 cycles).
 ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
-# Vector operations the method needs per visible pair in every attention kernel: the
-# scaled shift of the score (one FMA), its exponential, and one more (the row sum in
-# the forward, the product P (dP - delta) in the backward).
-ALU_OPS_PER_PAIR = 3
+# Vector work the method needs per visible (query, key) pair, in full-rate issue slots:
+# the scaled shift of the score (one FMA), its exponential (v_exp_f32 occupies a SIMD
+# for 8 cycles, two slots: the SQ counters' VALU cycles per instruction fit
+# 4 (1 - f) + 8 f with f the transcendental share, on every profiled kernel), then
+#   forward, bf16: the row-sum add and half a conversion (v_cvt_pk_bf16_f32 rounds two
+#     values of P for the PV MFMA)                                   1 + 2 + 1 + 0.5
+#   forward, fp32: the row-sum add and the row-max pass                1 + 2 + 1 + 1
+#   dK/dV: the product P (dP - delta) and two half conversions (P, dS) 1 + 2 + 1 + 1
+#   dQ: the product P (dP - delta) and half a conversion (dS)        1 + 2 + 1 + 0.5
+ALU_SLOTS_PER_PAIR = {"fwd_kernel": 4.5, "fwd_kernel_f32": 5.0, "bwd_dkdv_kernel": 5.0,
+                      "bwd_dq_kernel": 4.5}
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "ring_context_parallelism_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -172,7 +179,9 @@ def pmc_summary(root, workload):
     cmd = ("cd /tmp && timeout -s KILL 240 rocprofv3 --pmc {c} --output-format csv -d <out>/{d} "
            "-o run -- python3 <repo>/bench.py {a}")
     run_args = _profiled_args(workload)
-    lines = [f"# HBM traffic per dispatch: {workload} workload", "",
+    title = ("the HBM-bound helper kernels (standalone LSE merge, backward delta) at the "
+             "zig-zag share's shape" if workload == "aux" else f"{workload} workload")
+    lines = [f"# HBM traffic per dispatch: {title}", "",
              "Commands (one counter per run, on one MI355X):", "", "```"]
     for c, d, a in (("FETCH_SIZE", "pmc_fetch", run_args),
                     ("WRITE_SIZE", "pmc_write", run_args),
@@ -222,6 +231,8 @@ SQ_PASSES = (
     "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_MISC SQ_WAIT_ANY SQ_BUSY_CU_CYCLES",
     "SQ_INSTS_VALU SQ_ACTIVE_INST_ANY SQ_WAIT_INST_ANY SQ_INST_LEVEL_LDS SQ_INSTS_SALU "
     "SQ_ACTIVE_INST_SCA SQ_INSTS_VMEM SQ_WAVES",
+    "SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_VALU_FMA_F32 SQ_INSTS_VALU_ADD_F32 SQ_INSTS_VALU_MUL_F32 "
+    "SQ_INSTS_VALU_CVT SQ_INSTS_VALU_INT32 SQ_VALU_MFMA_COEXEC_CYCLES SQ_BUSY_CU_CYCLES",
 )
 
 
@@ -242,7 +253,8 @@ def sq_summary(root, workload, n_cu=256):
     cmd = ("cd /tmp && timeout -s KILL 200 rocprofv3 --pmc {c} --output-format csv -d <out>/cnt_{i} "
            "-o run -- python3 <repo>/bench.py {a}")
     lines = [f"# SQ counters per kernel: {workload} workload", "",
-             "Commands (three passes, at most 8 SQ counters each, on one MI355X):", "", "```"]
+             f"Commands ({len(SQ_PASSES)} passes, at most 8 SQ counters each, on one MI355X):",
+             "", "```"]
     lines += [cmd.format(c=c, i=i + 1, a=_profiled_args(workload)) for i, c in enumerate(SQ_PASSES)]
     lines += ["python3 <repo>/bench.py --sq-summary <out>", "```", "",
               "Cycle counters are summed over the chip (`SQ_BUSY_CU_CYCLES` over 256 CUs, "
@@ -251,11 +263,20 @@ def sq_summary(root, workload, n_cu=256):
               "clock = "
               "`SQ_BUSY_CU_CYCLES` / 256 / kernel duration.  VALU instructions per SIMD-cycle = "
               "`SQ_INSTS_VALU` / (4 `SQ_BUSY_CU_CYCLES`); waves per SIMD = `SQ_WAVE_CYCLES` / "
-              "`SQ_BUSY_CU_CYCLES` (`SQ_WAVE_CYCLES` counts in units of 4 cycles).", "",
+              "`SQ_BUSY_CU_CYCLES` (`SQ_WAVE_CYCLES` counts in units of 4 cycles).  VALU busy = "
+              "`SQ_ACTIVE_INST_VALU` / `SQ_BUSY_CU_CYCLES` (quad-cycles over the chip's 4 "
+              "SIMDs per CU: the share of SIMD cycles a VALU instruction occupies, the "
+              "vendor's VALUBusy); VALU cycles per instruction = 4 `SQ_ACTIVE_INST_VALU` / "
+              "`SQ_INSTS_VALU` (4 for a stream of full-rate wave64 instructions).", "",
               "| kernel | duration (ms, under counters) | effective clock (GHz) | MFMA busy | LDS busy "
               "| LDS bank-conflict share | VALU / MFMA | LDS / MFMA | SALU / MFMA | wait-any / wave cycles "
-              "| VALU instr per SIMD-cycle | waves per SIMD |",
-              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+              "| VALU instr per SIMD-cycle | waves per SIMD | VALU busy |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    mix_lines = ["", "VALU instruction mix (shares of `SQ_INSTS_VALU`) and VALU cycles per "
+                 "instruction:", "",
+                 "| kernel | transcendental f32 | FMA f32 | add f32 | mul f32 | convert | int32 | "
+                 "other | VALU cycles per instruction | MFMA + VALU co-issue / MFMA busy |",
+                 "|---|---|---|---|---|---|---|---|---|---|"]
     logged = _logged_hashes(*[os.path.join(root, f"cnt_{i + 1}.log")
                               for i in range(len(SQ_PASSES))]) or {}
     data = {"workload": workload, "kernels": {}}
@@ -263,21 +284,38 @@ def sq_summary(root, workload, n_cu=256):
         m = {k: sum(v) / len(v) for k, v in c.items()}
         t = sum(dur[key].values()) / len(dur[key])
         busy = m["SQ_BUSY_CU_CYCLES"]
+        valu_busy = m["SQ_ACTIVE_INST_VALU"] / busy
         data["kernels"][key] = {
             "name": KERNELS[key][0], "source_hash": logged.get(key),
             "mfma_busy": round(m["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * busy), 4),
             "effective_clock_ghz": round(busy / n_cu / t / 1e9, 3),
-            "lds_busy": round(m["SQ_LDS_IDX_ACTIVE"] / busy, 4)}
+            "lds_busy": round(m["SQ_LDS_IDX_ACTIVE"] / busy, 4),
+            "valu_busy": round(valu_busy, 4)}
+        if "SQ_INSTS_VALU_TRANS_F32" in m:
+            n = max(m["SQ_INSTS_VALU"], 1.0)
+            parts = [m[c] / n for c in ("SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_VALU_FMA_F32",
+                                        "SQ_INSTS_VALU_ADD_F32", "SQ_INSTS_VALU_MUL_F32",
+                                        "SQ_INSTS_VALU_CVT", "SQ_INSTS_VALU_INT32")]
+            cpi = 4 * m["SQ_ACTIVE_INST_VALU"] / max(n, 1)
+            coex = m["SQ_VALU_MFMA_COEXEC_CYCLES"] / max(m["SQ_VALU_MFMA_BUSY_CYCLES"] / 4, 1)
+            data["kernels"][key].update(valu_trans_share=round(parts[0], 4),
+                                        valu_cycles_per_instr=round(cpi, 3))
+            mix_lines.append(f"| `{KERNELS[key][0]}` | " + " | ".join(f"{x:.3f}" for x in parts)
+                             + f" | {max(0.0, 1 - sum(parts)):.3f} | {cpi:.2f} | {coex:.3f} |")
+        per_mfma = (lambda c: f"{m[c] / m['SQ_INSTS_MFMA']:.2f}" if m["SQ_INSTS_MFMA"] > 0
+                    else "-")
         lines.append(
             f"| `{KERNELS[key][0]}` | {t * 1e3:.2f} | {busy / n_cu / t / 1e9:.2f} | "
             f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * busy):.3f} | "
             f"{m['SQ_LDS_IDX_ACTIVE'] / busy:.3f} | "
             f"{m['SQ_LDS_BANK_CONFLICT'] / max(m['SQ_LDS_IDX_ACTIVE'], 1):.3f} | "
-            f"{m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f} | "
-            f"{m['SQ_INSTS_LDS'] / m['SQ_INSTS_MFMA']:.2f} | "
-            f"{m['SQ_INSTS_SALU'] / m['SQ_INSTS_MFMA']:.2f} | "
+            f"{per_mfma('SQ_INSTS_VALU')} | {per_mfma('SQ_INSTS_LDS')} | "
+            f"{per_mfma('SQ_INSTS_SALU')} | "
             f"{m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.3f} | "
-            f"{m['SQ_INSTS_VALU'] / (4 * busy):.3f} | {m['SQ_WAVE_CYCLES'] / busy:.2f} |")
+            f"{m['SQ_INSTS_VALU'] / (4 * busy):.3f} | {m['SQ_WAVE_CYCLES'] / busy:.2f} | "
+            f"{valu_busy:.3f} |")
+    if len(mix_lines) > 5:
+        lines += mix_lines
     lines += ["", "Read by `bench.py`, which attaches a kernel's figures to its `roofline` only "
               "while the `source_hash` printed by the profiled runs matches the current "
               "sources:", "", "```json", json.dumps(data, indent=1), "```", ""]
@@ -409,22 +447,23 @@ def measured_counters(workload, key):
     k = data["kernels"].get(key)
     if k is None or data["workload"] != workload or k["source_hash"] != source_hash(KERNELS[key][1]):
         return None
-    return {f: k[f] for f in ("mfma_busy", "effective_clock_ghz", "lds_busy")}
+    return {f: k[f] for f in ("mfma_busy", "effective_clock_ghz", "lds_busy", "valu_busy")
+            if f in k}
 
 
-def roofline(flop, pairs, launch_ms, mfma_peak):
+def roofline(flop, pairs, launch_ms, mfma_peak, alu_slots):
     """The roof a kernel sits closer to: the matrix cores (its algorithmic FLOP against
-    the dense MFMA peak of its dtype) or the vector ALU (ALU_OPS_PER_PAIR per visible
-    pair against ALU_PEAK_TOPS; small head dims, where the per-score softmax work
-    dominates).  The other fraction is reported alongside."""
+    the dense MFMA peak of its dtype) or the vector ALU (alu_slots full-rate issue slots
+    per visible pair against ALU_PEAK_TOPS; small head dims, where the per-score softmax
+    work dominates).  The other fraction is reported alongside."""
     achieved = flop / (launch_ms * 1e-3) / 1e12
-    alu_ops = ALU_OPS_PER_PAIR * pairs
+    alu_ops = alu_slots * pairs
     alu_achieved = alu_ops / (launch_ms * 1e-3) / 1e12
     if alu_achieved / ALU_PEAK_TOPS > achieved / mfma_peak:
         return {"bound": "alu", "achieved": round(alu_achieved, 3),
                 "peak": round(ALU_PEAK_TOPS, 2), "unit": "TOP/s",
                 "frac": round(alu_achieved / ALU_PEAK_TOPS, 4), "ops_per_launch": alu_ops,
-                "mfma_frac": round(achieved / mfma_peak, 4)}
+                "slots_per_pair": alu_slots, "mfma_frac": round(achieved / mfma_peak, 4)}
     return {"bound": "mfma", "achieved": round(achieved, 3), "peak": mfma_peak,
             "unit": "TFLOP/s", "frac": round(achieved / mfma_peak, 4), "flop_per_launch": flop,
             "alu_frac": round(alu_achieved / ALU_PEAK_TOPS, 4)}
@@ -975,7 +1014,8 @@ def main():
                                  q_ms / len(steps))
     name = max(kern, key=lambda k: kern[k][0])
     _, per_launch_flop, launch_ms = kern[name]
-    res["roofline"] = roofline(per_launch_flop, sum(pairs_bh) / len(steps), launch_ms, peak)
+    res["roofline"] = roofline(per_launch_flop, sum(pairs_bh) / len(steps), launch_ms, peak,
+                               ALU_SLOTS_PER_PAIR[name])
     res["roofline"].update({"traffic": measured_traffic(w.name, name), "kernel": name,
                             "avg_launch_ms": round(launch_ms, 4)})
     counters = measured_counters(w.name, name)

@@ -101,15 +101,19 @@ def test_counter_figures_only_for_the_sources_they_were_taken_on(tmp_path, monke
 def test_roofline_picks_the_closer_roof():
     # d = 128, bf16: 4 d = 512 FLOP per pair against the matrix peak -- MFMA-bound
     pairs = 3.436e10
-    r = bench.roofline(512 * pairs, pairs, 14.0, bench.BF16_PEAK_TFLOPS)
+    slots = bench.ALU_SLOTS_PER_PAIR["fwd_kernel"]
+    r = bench.roofline(512 * pairs, pairs, 14.0, bench.BF16_PEAK_TFLOPS, slots)
     assert r["bound"] == "mfma" and abs(r["frac"] - 512 * pairs / 14e-3 / 1e12 / 2516.6) < 1e-4
     assert r["alu_frac"] < r["frac"]
-    # d = 24: 96 FLOP per pair; the softmax's 3 vector operations per pair bind first
+    # d = 24: 96 FLOP per pair; the softmax's 4.5 vector issue slots per pair bind first
     pairs = 2.8125e10
-    r = bench.roofline(96 * pairs, pairs, 4.6, bench.BF16_PEAK_TFLOPS)
-    assert r["bound"] == "alu" and r["unit"] == "TOP/s"
-    assert abs(r["achieved"] - 3 * pairs / 4.6e-3 / 1e12) < 1e-2
+    r = bench.roofline(96 * pairs, pairs, 4.6, bench.BF16_PEAK_TFLOPS, slots)
+    assert r["bound"] == "alu" and r["unit"] == "TOP/s" and r["slots_per_pair"] == 4.5
+    assert abs(r["achieved"] - 4.5 * pairs / 4.6e-3 / 1e12) < 1e-2
     assert abs(bench.ALU_PEAK_TOPS - 39.3216) < 1e-3 and r["mfma_frac"] < r["frac"]
+    # every kernel the bench can name has a vector cost
+    assert set(bench.ALU_SLOTS_PER_PAIR) == {"fwd_kernel", "fwd_kernel_f32", "bwd_dkdv_kernel",
+                                              "bwd_dq_kernel"}
 
 
 def test_cpu_baseline_covers_the_whole_head_when_it_fits():
