@@ -183,18 +183,21 @@ ra_status_t ra_block_attn_bwd(const ra_problem_t* prob, const void* q, int32_t q
 /*
  * The two halves of ra_block_attn_bwd, for callers that schedule them apart (in a
  * multi-device ring dQ stays with the query owner while dK and dV travel with the
- * KV chunk).  Same arguments, layouts and accumulation semantics as
- * ra_block_attn_bwd; ra_block_attn_bwd_dkdv accumulates dk and dv only,
- * ra_block_attn_bwd_dq accumulates dq only.  Neither uses atomics: each output
- * element has one writer, so results are deterministic.
+ * KV chunk).  Same arguments and layouts as ra_block_attn_bwd;
+ * ra_block_attn_bwd_dkdv produces dk and dv only, ra_block_attn_bwd_dq dq only.
+ * mode RA_MERGE adds the step's gradients into the buffers (as ra_block_attn_bwd);
+ * mode RA_WRITE stores them, every element included (zeros where no pair is
+ * visible), so the buffers need no zero-fill when this step is the first to reach
+ * them (in a ring, every KV chunk is visited once; dq by every step).  Neither uses
+ * atomics: each output element has one writer, so results are deterministic.
  */
 ra_status_t ra_block_attn_bwd_dkdv(const ra_problem_t* prob, const void* q, int32_t q_chunk,
                                    const void* k, const void* v, int32_t kv_chunk,
                                    const void* dout, const float* lse, const float* delta,
-                                   float* dk, float* dv, hipStream_t stream);
+                                   float* dk, float* dv, int32_t mode, hipStream_t stream);
 ra_status_t ra_block_attn_bwd_dq(const ra_problem_t* prob, const void* q, int32_t q_chunk,
                                  const void* k, const void* v, int32_t kv_chunk, const void* dout,
-                                 const float* lse, const float* delta, float* dq,
+                                 const float* lse, const float* delta, float* dq, int32_t mode,
                                  hipStream_t stream);
 
 /*
@@ -216,10 +219,11 @@ ra_status_t ra_bwd_prepare(const ra_problem_t* prob, const void* out, const void
 ra_status_t ra_ring_bwd_workspace_size(const ra_problem_t* prob, size_t* bytes);
 
 /*
- * The ring driver, backward, for rank `rank`: runs ra_bwd_prepare (delta into
- * ws; dq and every dk_chunks[c], dv_chunks[c] zero-filled), then accumulates
- * every step with a visible pair, in ring order.  out / lse are the forward's
- * results for this rank.  dk_chunks and dv_chunks are HOST arrays of p device
+ * The ring driver, backward, for rank `rank`: delta (as ra_bwd_delta) into ws,
+ * then every step with a visible pair, in ring order: each KV chunk's dk/dv is
+ * stored by its step (RA_WRITE), dq is stored by the first live step and added by
+ * the others; buffers no live step reaches are zero-filled.  No output needs to be
+ * initialised by the caller.  out / lse are the forward's results for this rank.  dk_chunks and dv_chunks are HOST arrays of p device
  * pointers (fp32 [B, Hkv, L, D]); the result is this rank's share of the
  * gradients (its queries only).  ws: at least ra_ring_bwd_workspace_size()
  * bytes, 256-byte aligned.  Supported: bf16.

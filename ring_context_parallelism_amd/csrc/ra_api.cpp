@@ -438,9 +438,10 @@ static ra::BwdArgs bwd_args(const ra_problem_t* prob, const void* q, int cq, con
 static ra_status_t block_bwd(const ra_problem_t* prob, const void* q, int32_t q_chunk,
                              const void* k, const void* v, int32_t kv_chunk, const void* dout,
                              const float* lse, const float* delta, float* dq, float* dk,
-                             float* dv, int which, hipStream_t stream) {
+                             float* dv, int which, int32_t mode, hipStream_t stream) {
   RA_TRY(check_problem(prob));
   RA_TRY(bwd_supported(prob));
+  if (mode != RA_WRITE && mode != RA_MERGE) return fail(RA_ERR_UNSUPPORTED, "unknown mode %d", mode);
   RA_TRY(check_chunk(prob, q_chunk, "q_chunk"));
   RA_TRY(check_chunk(prob, kv_chunk, "kv_chunk"));
   RA_TRY(check_ptr(q, "q"));
@@ -454,9 +455,20 @@ static ra_status_t block_bwd(const ra_problem_t* prob, const void* q, int32_t q_
   }
   if (lse == nullptr || delta == nullptr) return fail(RA_ERR_NULL, "lse or delta is NULL");
   const ra::LayoutMap m = make_map(prob);
-  if (!step_live(prob, m, q_chunk, kv_chunk)) return ok();  // nothing visible: no-op
   ra::BwdArgs a = bwd_args(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dq, dk, dv);
-  hipError_t e = ra::launch_bwd(prob->dtype, (int)prob->head_dim_padded, a, which, stream);
+  a.write = mode == RA_WRITE;
+  hipError_t e = hipSuccess;
+  if (step_live(prob, m, q_chunk, kv_chunk)) {
+    e = ra::launch_bwd(prob->dtype, (int)prob->head_dim_padded, a, which, stream);
+  } else if (a.write) {  // nothing visible: the step's gradients are zero
+    const int64_t L = prob->seq_total / prob->world, D = prob->head_dim_padded;
+    if (which & 2) e = ra::launch_fill_f32(dq, prob->batch * prob->heads_q * L * D, 0.0f, stream);
+    if (e == hipSuccess && (which & 1)) {
+      const int64_t n = prob->batch * prob->heads_kv * L * D;
+      e = ra::launch_fill_f32(dk, n, 0.0f, stream);
+      if (e == hipSuccess) e = ra::launch_fill_f32(dv, n, 0.0f, stream);
+    }
+  }
   if (e != hipSuccess) return hip_fail(e, "ra_block_attn_bwd launch");
   return ok();
 }
@@ -465,23 +477,24 @@ ra_status_t ra_block_attn_bwd(const ra_problem_t* prob, const void* q, int32_t q
                               const void* k, const void* v, int32_t kv_chunk, const void* dout,
                               const float* lse, const float* delta, float* dq, float* dk,
                               float* dv, hipStream_t stream) {
-  return block_bwd(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dq, dk, dv, 3, stream);
+  return block_bwd(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dq, dk, dv, 3, RA_MERGE,
+                   stream);
 }
 
 ra_status_t ra_block_attn_bwd_dkdv(const ra_problem_t* prob, const void* q, int32_t q_chunk,
                                    const void* k, const void* v, int32_t kv_chunk,
                                    const void* dout, const float* lse, const float* delta,
-                                   float* dk, float* dv, hipStream_t stream) {
-  return block_bwd(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, nullptr, dk, dv, 1,
+                                   float* dk, float* dv, int32_t mode, hipStream_t stream) {
+  return block_bwd(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, nullptr, dk, dv, 1, mode,
                    stream);
 }
 
 ra_status_t ra_block_attn_bwd_dq(const ra_problem_t* prob, const void* q, int32_t q_chunk,
                                  const void* k, const void* v, int32_t kv_chunk, const void* dout,
-                                 const float* lse, const float* delta, float* dq,
+                                 const float* lse, const float* delta, float* dq, int32_t mode,
                                  hipStream_t stream) {
   return block_bwd(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dq, nullptr, nullptr, 2,
-                   stream);
+                   mode, stream);
 }
 
 ra_status_t ra_ring_bwd_workspace_size(const ra_problem_t* prob, size_t* bytes) {
@@ -520,16 +533,33 @@ ra_status_t ra_ring_bwd(const ra_problem_t* prob, int32_t rank, const void* q,
   if (((uintptr_t)ws & 255u) != 0) return fail(RA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   const ra::LayoutMap m = make_map(prob);
   float* delta = (float*)ws;
-  const int64_t D = prob->head_dim_padded;
-  RA_TRY(ra_bwd_prepare(prob, out, dout, delta, dq, dk_chunks, dv_chunks, stream));
-  for (int s = 0; s < prob->world; ++s) {
+  const int64_t L = prob->seq_total / prob->world, D = prob->head_dim_padded;
+  RA_TRY(ra_bwd_delta(prob, out, dout, delta, stream));
+  // Every chunk is visited once, so its dK, dV are stored (not added) by its step; dQ is
+  // stored by the first live step and added by the others.  Buffers no step reaches are
+  // zero-filled.
+  bool dq_written = false;
+  hipError_t e = hipSuccess;
+  for (int s = 0; s < prob->world && e == hipSuccess; ++s) {
     const int c = ((rank - s) % prob->world + prob->world) % prob->world;
-    if (!step_live(prob, m, rank, c)) continue;
+    if (!step_live(prob, m, rank, c)) {
+      const int64_t n = prob->batch * prob->heads_kv * L * D;
+      e = ra::launch_fill_f32(dk_chunks[c], n, 0.0f, stream);
+      if (e == hipSuccess) e = ra::launch_fill_f32(dv_chunks[c], n, 0.0f, stream);
+      continue;
+    }
     ra::BwdArgs a = bwd_args(prob, q, rank, k_chunks[c], v_chunks[c], c, dout, lse, delta, dq,
                              dk_chunks[c], dv_chunks[c]);
-    const hipError_t e = ra::launch_bwd(prob->dtype, (int)D, a, 3, stream);
-    if (e != hipSuccess) return hip_fail(e, "ra_ring_bwd launch");
+    a.write = 1;
+    e = ra::launch_bwd(prob->dtype, (int)D, a, 1, stream);
+    if (e != hipSuccess) break;
+    a.write = dq_written ? 0 : 1;
+    e = ra::launch_bwd(prob->dtype, (int)D, a, 2, stream);
+    dq_written = true;
   }
+  if (e == hipSuccess && !dq_written)
+    e = ra::launch_fill_f32(dq, prob->batch * prob->heads_q * L * D, 0.0f, stream);
+  if (e != hipSuccess) return hip_fail(e, "ra_ring_bwd launch");
   return ok();
 }
 

@@ -248,7 +248,22 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int n_qt = (t_end + kKvBQ - 1) / kKvBQ;
   const int per_head = n_qt - qt_first;
   const int n_iter = per_head > 0 ? per_head * a.group : 0;
-  if (n_iter == 0) return;  // no query of this chunk sees these keys
+  if (n_iter == 0) {  // no query of this chunk sees these keys: zero gradient
+    if (a.write) {
+      const f32x4 z = {};
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        if (!key_ok[x]) continue;
+        const int64_t grow = (((int64_t)b * a.Hkv + g) * L + key[x]) * D;
+#pragma unroll
+        for (int n = 0; n < NDT; ++n) {
+          *(f32x4*)(a.dk + grow + n * 16 + grp * 4) = z;
+          *(f32x4*)(a.dv + grow + n * 16 + grp * 4) = z;
+        }
+      }
+    }
+    return;
+  }
 
   f32x4 dv_t[NDT][2], dk_t[NDT][2];  // [head-dim tile][key tile]
 #pragma unroll
@@ -449,8 +464,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     if (it + 1 < n_iter) step(it + 1, q1, do1, ls1, dl1, q0, do0, ls0, dl0);
   }
 
-  // Add into dK and dV; accumulator row r of head-dim tile n is d = 16 n + 4 grp + r
-  // of this lane's key.
+  // Store or add into dK and dV; accumulator row r of head-dim tile n is
+  // d = 16 n + 4 grp + r of this lane's key.
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     if (!key_ok[x]) continue;
@@ -459,8 +474,13 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     for (int n = 0; n < NDT; ++n) {
       f32x4* pk = (f32x4*)(a.dk + grow + n * 16 + grp * 4);
       f32x4* pv = (f32x4*)(a.dv + grow + n * 16 + grp * 4);
-      *pk = *pk + dk_t[n][x] * a.scale;
-      *pv = *pv + dv_t[n][x];
+      if (a.write) {
+        *pk = dk_t[n][x] * a.scale;
+        *pv = dv_t[n][x];
+      } else {
+        *pk = *pk + dk_t[n][x] * a.scale;
+        *pv = *pv + dv_t[n][x];
+      }
     }
   }
 }
@@ -672,8 +692,9 @@ __global__ __launch_bounds__((QCfg<D, PACKED>::NT), (QCfg<D, PACKED>::NW == 4 ? 
     if (j + 1 < n_tiles) tile(j + 1, k1, v1, k0, v0);
   }
 
-  // dQ[q][d] += scale * dQ^T[d][q]; accumulator row r of tile n is d = 16 n + 4 grp + r.
-  if (n_tiles > j0) {
+  // dQ[q][d] (+)= scale * dQ^T[d][q]; accumulator row r of tile n is d = 16 n + 4 grp + r.
+  // A row that sees no key of this chunk adds nothing, or stores zeros in write mode.
+  if (n_tiles > j0 || a.write) {
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       if (tq[x] >= L) continue;
@@ -681,7 +702,11 @@ __global__ __launch_bounds__((QCfg<D, PACKED>::NT), (QCfg<D, PACKED>::NW == 4 ? 
 #pragma unroll
       for (int n = 0; n < NDT; ++n) {
         f32x4* p = (f32x4*)(dqr + n * 16 + grp * 4);
-        *p = *p + dq_t[n][x] * a.scale;
+        if (a.write) {
+          *p = dq_t[n][x] * a.scale;
+        } else {
+          *p = *p + dq_t[n][x] * a.scale;
+        }
       }
     }
   }

@@ -189,6 +189,8 @@ struct BwdArgs {
   float* dv;                    // [B, Hkv, L, D]  (+=)
   const int32_t* seg;           // packed-document boundaries [B, seg_n], or nullptr
   int32_t seg_n;
+  int32_t write;                // 1: store the step's dq / dk, dv (every element, zeros
+                                // included) instead of adding to them
 };
 
 // Launchers (defined in the .hip files).  Return the hipError_t of the launch.

@@ -84,8 +84,9 @@ def lib():
             "ra_bwd_delta": [_PROB, _P, _P, _P, _P],
             "ra_bwd_prepare": [_PROB, _P, _P, _P, _P, _P, _P, _P],
             "ra_block_attn_bwd": [_PROB, _P, _I32, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P],
-            "ra_block_attn_bwd_dkdv": [_PROB, _P, _I32, _P, _P, _I32, _P, _P, _P, _P, _P, _P],
-            "ra_block_attn_bwd_dq": [_PROB, _P, _I32, _P, _P, _I32, _P, _P, _P, _P, _P],
+            "ra_block_attn_bwd_dkdv": [_PROB, _P, _I32, _P, _P, _I32, _P, _P, _P, _P, _P, _I32,
+                                       _P],
+            "ra_block_attn_bwd_dq": [_PROB, _P, _I32, _P, _P, _I32, _P, _P, _P, _P, _I32, _P],
             "ra_ring_bwd_workspace_size": [_PROB, ctypes.POINTER(_SZ)],
             "ra_ring_bwd": [_PROB, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
             "ra_ring_bwd_noalloc": [_PROB, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
@@ -218,16 +219,17 @@ def ra_block_attn_bwd(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dq, dk
 
 
 def ra_block_attn_bwd_dkdv(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dk, dv,
-                           stream=None):
+                           mode=RA_MERGE, stream=None):
     _launched(lib().ra_block_attn_bwd_dkdv(ctypes.byref(prob), _ptr(q), q_chunk, _ptr(k), _ptr(v),
                                         kv_chunk, _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dk),
-                                        _ptr(dv), _stream(stream)))
+                                        _ptr(dv), mode, _stream(stream)))
 
 
-def ra_block_attn_bwd_dq(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dq, stream=None):
+def ra_block_attn_bwd_dq(prob, q, q_chunk, k, v, kv_chunk, dout, lse, delta, dq, mode=RA_MERGE,
+                         stream=None):
     _launched(lib().ra_block_attn_bwd_dq(ctypes.byref(prob), _ptr(q), q_chunk, _ptr(k), _ptr(v),
                                       kv_chunk, _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq),
-                                      _stream(stream)))
+                                      mode, _stream(stream)))
 
 
 def ra_ring_bwd_workspace_size(prob) -> int:

@@ -173,6 +173,10 @@ def test_call_validation():
                       FAKE, 0) == ra.RA_ERR_UNSUPPORTED
     assert _status_of(ra.ra_ring_bwd, p, 0, FAKE, ks, ks, FAKE, FAKE, FAKE, FAKE, ks, ks,
                       FAKE, 8, 0) == ra.RA_ERR_WORKSPACE
+    # the backward halves take RA_WRITE or RA_MERGE only
+    for half, outs in ((ra.ra_block_attn_bwd_dkdv, (FAKE, FAKE)), (ra.ra_block_attn_bwd_dq, (FAKE,))):
+        assert _status_of(half, p, FAKE, 0, FAKE, FAKE, 0, FAKE, FAKE, FAKE, *outs, 7,
+                          0) == ra.RA_ERR_UNSUPPORTED
     # ra_bwd_prepare checks every pointer before its first launch
     prep = ra.ra_bwd_prepare
     assert _status_of(prep, p, FAKE, FAKE, FAKE, 0, ks, ks, 0) == ra.RA_ERR_NULL

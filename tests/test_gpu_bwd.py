@@ -198,8 +198,10 @@ def test_full_size_backward_two_heads_elementwise():
 
 
 def test_split_entry_points_match_combined():
-    """ra_block_attn_bwd_dkdv + ra_block_attn_bwd_dq equal ra_block_attn_bwd exactly
-    (no atomics anywhere: every output element has a single writer)."""
+    """ra_block_attn_bwd_dkdv + ra_block_attn_bwd_dq in RA_MERGE mode add exactly what
+    ra_block_attn_bwd adds (no atomics anywhere: every output element has a single
+    writer); in RA_WRITE mode they store the same values, bit for bit, into NaN-filled
+    buffers (every element written); a step with no visible pair stores zeros."""
     dev = need_gpu()
     w = SMALL[2]
     arrays = generate(w)
@@ -212,10 +214,34 @@ def test_split_entry_points_match_combined():
     for c in range(w.world):
         dq1, dk1, dv1 = mk(w.heads_q), mk(w.heads_kv), mk(w.heads_kv)
         dq2, dk2, dv2 = mk(w.heads_q), mk(w.heads_kv), mk(w.heads_kv)
+        guard = Guarded()
+        dq3 = guard((w.batch, w.heads_q, L, D), torch.float32, dev)
+        dk3 = guard((w.batch, w.heads_kv, L, D), torch.float32, dev)
+        dv3 = guard((w.batch, w.heads_kv, L, D), torch.float32, dev)
         args = (share.prob, share.q, 1, share.k_chunks[c], share.v_chunks[c], c, share.do, lse,
                 delta)
         ra.ra_block_attn_bwd(*args, dq1, dk1, dv1)
-        ra.ra_block_attn_bwd_dkdv(*args, dk2, dv2)
-        ra.ra_block_attn_bwd_dq(*args, dq2)
+        ra.ra_block_attn_bwd_dkdv(*args, dk2, dv2, mode=ra.RA_MERGE)
+        ra.ra_block_attn_bwd_dq(*args, dq2, mode=ra.RA_MERGE)
+        ra.ra_block_attn_bwd_dkdv(*args, dk3, dv3, mode=ra.RA_WRITE)
+        ra.ra_block_attn_bwd_dq(*args, dq3, mode=ra.RA_WRITE)
         torch.cuda.synchronize()
+        guard.check(f"write mode chunk {c}")
         assert torch.equal(dq1, dq2) and torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+        assert torch.equal(dq1, dq3) and torch.equal(dk1, dk3) and torch.equal(dv1, dv3)
+    # rank 0 of a contiguous causal share sees nothing of chunk 1: RA_WRITE stores zeros
+    w = SMALL[1]
+    arrays = generate(w)
+    share = staging.stage(w, arrays, dev, rank=0)
+    out, lse = staging.ring_forward(share, w, rank=0)
+    L, D = w.chunk_len, w.head_dim_padded
+    delta = torch.empty((w.batch, w.heads_q, L), dtype=torch.float32, device=dev)
+    ra.ra_bwd_delta(share.prob, out, share.do, delta)
+    nan = lambda H: torch.full((w.batch, H, L, D), float("nan"), device=dev)
+    dq, dk, dv = nan(w.heads_q), nan(w.heads_kv), nan(w.heads_kv)
+    args = (share.prob, share.q, 0, share.k_chunks[1], share.v_chunks[1], 1, share.do, lse, delta)
+    ra.ra_block_attn_bwd_dkdv(*args, dk, dv, mode=ra.RA_WRITE)
+    ra.ra_block_attn_bwd_dq(*args, dq, mode=ra.RA_WRITE)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.count_nonzero(torch.nan_to_num(t, nan=1.0)).item() == 0
