@@ -70,16 +70,21 @@ __device__ inline bf16x8 cat(s16x4 a, s16x4 b) {
 //
 // LDS serves 16 lanes x 16 bytes per clock from 64 four-byte banks.
 //
-// Padded tile (read both ways): an odd row stride (3, 13 or 19 sixteen-byte chunks)
-// keeps every address a per-lane base plus a compile-time offset and, with the row
-// order rho16 below, makes the transpose reads conflict free.
+// Line tile (32 rows read both ways, by 16-byte row reads and by transpose reads):
+// the 16-byte chunk c of logical row m lives in slot
+//   16 (CH (m / 16) + c) + ((m mod 16) xor 8 (c mod 2)),
+// so each 256-byte line holds chunk c of 16 rows, with no padding: a 32-row tile is
+// exactly two 1 KB direct-to-LDS loads per wave of a 4-wave workgroup.  A transpose
+// read serves 32 lanes, 8 rows x 32 bytes (chunks 2n, 2n + 1); the xor by 8 on odd
+// chunks puts them in 16 distinct bank groups, which a probe kernel measured conflict
+// free.  The 16-byte row reads take two passes: on this chip they are conflict free
+// only when every lane also reads a different 256-byte line (measured), and no
+// placement that steps by compile-time offsets in both directions gives that within
+// the tile's own lines.  Every address is a per-lane base plus a compile-time offset.
 template <int COLS>
-struct Pad {
-  static constexpr int CH = COLS / 8;
-  static constexpr int SCH = CH <= 3 ? 3 : (CH <= 13 ? 13 : (CH <= 19 ? 19 : 29));
-  static constexpr int PS = SCH * 8;  // row stride in elements
-  static constexpr int slots(int rows) { return ((rows * SCH + 63) / 64) * 64; }
-};
+__device__ inline int line_slot(int m, int c) {
+  return 16 * ((COLS / 8) * (m >> 4) + c) + ((m & 15) ^ (8 * (c & 1)));
+}
 
 // Swizzled tile (16-byte row reads only): XOR the chunk with the row's index among
 // the rows that share one 256-byte bank window, so 16 consecutive rows at one
@@ -95,57 +100,41 @@ __device__ inline int xoff(int r, int col) {  // element offset of column col (m
   return r * COLS + ((((col >> 3) ^ xsw<COLS>(r))) << 3);
 }
 
-// Tile row order of the 16x16x32 operands: logical row m = 16 h + 4 g + k (h: query
-// half, g: transpose-read lane group, k: row within the group) lives in tile row
-// 16 h + 2 (4 (g & 1) + k) + (g >> 1).  A transpose read (lane groups {0,1} or
-// {2,3}, 8 rows x 2 chunks) then touches 8 rows of one parity, which the odd padded
-// stride puts in 16 distinct bank groups: conflict free.  The 16-byte row reads of
-// such a tile take two passes: on this chip a 16-byte read is conflict free only if
-// every quad of consecutive lanes reads two aligned 32-byte blocks, and a quad's rows
-// lie inside one transpose block, which needs them in 4 distinct blocks (measured;
-// no row order satisfies both).
-__device__ inline int rho16(int m) {
-  const int g = (m >> 2) & 3;
-  return (m & 16) | ((((g & 1) << 2) | (m & 3)) << 1) | (g >> 1);
-}
-
-// Direct-to-LDS loads of rows r0..r0+ROWS-1 into a padded tile.  Pad slots, rows
-// past ROWS and rows past the resource end are zero-filled.
-template <int ROWS, int COLS, int NT>
-__device__ inline void dma_pad(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, int r0,
-                               __bf16* tile, int wave, int lane) {
-  using P = Pad<COLS>;
-  constexpr int SLOTS = P::slots(ROWS);
+// Direct-to-LDS loads of rows r0..r0+31 into a line tile: lane i of a load lands in
+// slot base + i and fetches the global chunk that belongs there.  Rows past the
+// resource end arrive as zeros.
+template <int COLS, int NT>
+__device__ inline void dma_lines(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, int r0,
+                                 __bf16* tile, int wave, int lane) {
+  constexpr int CH = COLS / 8;
+  constexpr int SLOTS = 32 * CH;
 #pragma unroll
   for (int it = 0; it < (SLOTS + NT - 1) / NT; ++it) {
     const int base = it * NT + wave * 64;
     if (SLOTS % NT != 0 && base >= SLOTS) break;  // wave-uniform
     const int slot = base + lane;
-    const int r = slot / P::SCH, c = slot % P::SCH;
-    const uint32_t off = (c < P::CH && r < ROWS)
-                             ? (uint32_t)(r0 + r) * row_bytes + (uint32_t)c * 16u
-                             : 0xFFFFFFF0u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + base * 8), 16, off, 0, 0, 0);
+    const int line = slot >> 4, c = line % CH;
+    const int m = 16 * (line / CH) + ((slot & 15) ^ (8 * (c & 1)));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + base * 8), 16,
+                                             (uint32_t)(r0 + m) * row_bytes + (uint32_t)c * 16u,
+                                             0, 0, 0);
   }
 }
 
-// Direct-to-LDS loads of rows r0..r0+ROWS-1 into a swizzled tile.  With PERM, tile
-// row p holds global row r0 + rho16(p) (32-row tiles).
-template <int ROWS, int COLS, int NT, bool PERM = false>
+// Direct-to-LDS loads of rows r0..r0+ROWS-1 into a swizzled tile.
+template <int ROWS, int COLS, int NT>
 __device__ inline void dma_xor(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, int r0,
                                __bf16* tile, int wave, int lane) {
   constexpr int CH = COLS / 8;
   constexpr int SLOTS = ROWS * CH;
   static_assert(SLOTS % 64 == 0, "tile must be whole wave loads");
-  static_assert(!PERM || ROWS == 32, "the row permutation is defined on 32-row tiles");
 #pragma unroll
   for (int it = 0; it < (SLOTS + NT - 1) / NT; ++it) {
     const int base = it * NT + wave * 64;
     if (SLOTS % NT != 0 && base >= SLOTS) break;  // wave-uniform
     const int slot = base + lane;
     const int r = slot / CH, pc = slot % CH;
-    const int gr = PERM ? rho16(r) : r;
-    const uint32_t off = (uint32_t)(r0 + gr) * row_bytes + (uint32_t)((pc ^ xsw<COLS>(r)) * 16);
+    const uint32_t off = (uint32_t)(r0 + r) * row_bytes + (uint32_t)((pc ^ xsw<COLS>(r)) * 16);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + base * 8), 16, off, 0, 0, 0);
   }
 }
@@ -171,9 +160,7 @@ template <int D, bool PACKED>
 __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NKK = D / 32;  // 32-wide head-dim steps of the S and dP contractions
   constexpr int NDT = D / 16;  // 16-row head-dim tiles of dK^T, dV^T
-  using PQ = Pad<D>;
-  constexpr int PS = PQ::PS;
-  constexpr int QEL = PQ::slots(kKvBQ) * 8;
+  constexpr int QEL = kKvBQ * D;  // line tile of 32 rows
 
   // Two distinct LDS objects per streamed tensor: the compiler can then prove the
   // loads into one never alias the reads of the other.
@@ -283,8 +270,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   int nt = t_lo;   // first row of the next DMA's tile
   int ct = t_lo;   // first row of the current step's tile
   auto dma_q = [&](__bf16* qn, __bf16* don) {
-    dma_pad<kKvBQ, D, kKvThreads>(make_rsrc(nq, (uint32_t)L * q_row), q_row, nt, qn, wave, lane);
-    dma_pad<kKvBQ, D, kKvThreads>(make_rsrc(no, (uint32_t)L * o_row), o_row, nt, don, wave, lane);
+    dma_lines<D, kKvThreads>(make_rsrc(nq, (uint32_t)L * q_row), q_row, nt, qn, wave, lane);
+    dma_lines<D, kKvThreads>(make_rsrc(no, (uint32_t)L * o_row), o_row, nt, don, wave, lane);
     nt += kKvBQ;
     if (nt >= t_hi) {
       nt = t_lo;
@@ -294,13 +281,13 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   };
   // Row statistics pass through registers one tile ahead of their LDS slots, so they
   // are stored transformed: wave 0 keeps LSE * log2 e (the exponent is one FMA),
-  // wave 1 keeps -delta (the dP accumulator starts from it).  Slot s holds logical
-  // row s: tile row (s & 32) + rho16(s & 31); rows past the chunk end read as 0,
+  // wave 1 keeps -delta (the dP accumulator starts from it).  Slot s holds query
+  // row s of the tile (the first kKvBQ slots are used); rows past the chunk end read as 0,
   // where Q = dO = 0 gives dS = dV = 0.  The LDS write of tile j's statistic comes
   // before the step's DMA issue and the load of tile j + 1's after it.
   const float* sst = (wave == 0 ? a.lse : a.delta) + ((int64_t)b * a.Hq + h0) * L;
   int st_row = t_lo;
-  const uint32_t st_lane = (uint32_t)((lane & 32) + rho16(lane & 31));
+  const uint32_t st_lane = (uint32_t)lane;
   float stat_next = 0.0f;
   auto stat_write = [&](float* lsn, float* dln) {
     if (wave == 0) lsn[lane] = stat_next * kLog2e;
@@ -330,16 +317,17 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
       for (int kk = 0; kk < NKK; ++kk)
         kreg[x][kk] = load_row8(kr, (uint32_t)key[x] * kv_row + (uint32_t)(kk * 64 + grp * 16));
   }
-  // A-operand rows of S and dP: logical rows 16 h + l16; transpose-read sources:
-  // logical rows 16 h + 4 grp + l16 / 4, columns 4 (l16 % 4) of a 16-column tile.
+  // Element offsets in the line tiles.  A-operand rows of S and dP: query rows
+  // 16 h + l16 at chunk 4 kk + grp (+512 kk); transpose-read sources: query rows
+  // 16 h + 4 grp + l16 / 4, columns 16 n + 4 (l16 % 4) (+256 n).
   int arow[2], trow[2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
-    arow[hf] = rho16(hf * 16 + l16) * PS + grp * 8;
-    trow[hf] = rho16(hf * 16 + grp * 4 + (l16 >> 2)) * PS + (l16 & 3) * 4;
+    arow[hf] = 8 * line_slot<D>(hf * 16 + l16, grp);
+    trow[hf] = 8 * line_slot<D>(hf * 16 + grp * 4 + (l16 >> 2), (l16 & 3) >> 1) + 4 * (l16 & 1);
   }
-  // Tile row of accumulator row r of query half hf: 16 hf + 2 r + goff.
-  const int goff = 8 * (grp & 1) + (grp >> 1);
+  // Query row of accumulator row r of half hf: 16 hf + r + goff.
+  const int goff = 4 * grp;
 
   auto step = [&](int it, const __bf16* qt, const __bf16* dot, const float* ls,
                   const float* dl, __bf16* qn, __bf16* don, float* lsn, float* dln) {
@@ -372,7 +360,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     for (int kk = 0; kk < NKK; ++kk) {
       bf16x8 qa[2];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) qa[hf] = *(const bf16x8*)(qt + arow[hf] + kk * 32);
+      for (int hf = 0; hf < 2; ++hf) qa[hf] = *(const bf16x8*)(qt + arow[hf] + kk * 512);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -386,7 +374,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
       for (int x = 0; x < 2; ++x)
         vbv[x] = *(const bf16x8*)(s_v + xoff<D>(krow[x], kk * 32 + grp * 8));
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) da[hf] = *(const bf16x8*)(dot + arow[hf] + kk * 32);
+      for (int hf = 0; hf < 2; ++hf) da[hf] = *(const bf16x8*)(dot + arow[hf] + kk * 512);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -395,11 +383,11 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     }
 
     // P = exp2(S*scale_log2 - LSE*log2 e), dS = P (dP - delta).  Accumulator row r
-    // of half hf is logical row 16 hf + 4 grp + r, tile row 16 hf + 2 r + goff.
+    // of half hf is query row 16 hf + 4 grp + r = 16 hf + r + goff of the tile.
     const int tq0 = t0;
     // dense problems: every query at or after q_lo sees the key (q_hi = L)
     const bool need_mask = tq0 < full_lo || (PACKED && tq0 + 32 > full_hi);
-    // Tile row c + goff (c = 16 hf + 2 r) is masked for key x when c < lo_c[x] or
+    // Query row c + goff (c = 16 hf + r) is masked for key x when c < lo_c[x] or
     // c >= hi_c[x]; outside the masked tiles the limits admit every row.
     int lo_c[2], hi_c[2];
 #pragma unroll
@@ -423,7 +411,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
         for (int x = 0; x < 2; ++x)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int c = 16 * hf + 2 * r;
+            const int c = 16 * hf + r;
             if (c < lo_c[x] || (PACKED && c >= hi_c[x])) s[hf][x][r] = 0.0f;
           }
     }
@@ -443,8 +431,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     __builtin_amdgcn_s_setprio(1);  // MFMA phase first when two waves compete for issue
 #pragma unroll
     for (int n = 0; n < NDT; ++n) {
-      const bf16x8 doa = cat(tr_read(dot + trow[0] + n * 16), tr_read(dot + trow[1] + n * 16));
-      const bf16x8 qta = cat(tr_read(qt + trow[0] + n * 16), tr_read(qt + trow[1] + n * 16));
+      const bf16x8 doa = cat(tr_read(dot + trow[0] + n * 256), tr_read(dot + trow[1] + n * 256));
+      const bf16x8 qta = cat(tr_read(qt + trow[0] + n * 256), tr_read(qt + trow[1] + n * 256));
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         dv_t[n][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(doa, pb[x], dv_t[n][x], 0, 0, 0);
@@ -507,9 +495,7 @@ __global__ __launch_bounds__((QCfg<D, PACKED>::NT), (QCfg<D, PACKED>::NW == 4 ? 
   constexpr int kQBM = QCfg<D, PACKED>::BM;
   constexpr int NKK = D / 32;  // 32-wide head-dim steps of the S^T and dP^T contractions
   constexpr int NDT = D / 16;  // 16-row head-dim tiles of dQ^T
-  using PK = Pad<D>;
-  constexpr int PS = PK::PS;
-  constexpr int KEL = PK::slots(kQBN) * 8;
+  constexpr int KEL = kQBN * D;  // line tile of 32 keys
   constexpr int VEL = kQBN * D;
   static_assert(kQBN == 32, "one 32-key contraction step per tile");
 
@@ -598,24 +584,22 @@ __global__ __launch_bounds__((QCfg<D, PACKED>::NT), (QCfg<D, PACKED>::NW == 4 ? 
 #pragma unroll
   for (int n = 0; n < NDT; ++n) dq_t[n][0] = dq_t[n][1] = f32x4{};
 
-  // Logical key l of a tile is global key j * kQBN + rho16(l).  The K tile, read
-  // both ways, keeps global row order, so key l sits in its row rho16(l); the V tile,
-  // read only by 16-byte row reads, is loaded permuted, so key l sits in its row l
-  // (with the XOR swizzle that keeps those reads conflict free).  A-operand rows of
-  // S^T and dP^T: logical keys 16 t + l16; transpose-read sources of K^T: logical keys
-  // 16 hf + 4 grp + l16 / 4, columns 4 (l16 % 4) of a 16-column tile.
+  // The K tile, read both ways, is a line tile; the V tile, read only by 16-byte row
+  // reads, is XOR-swizzled.  Element offsets in the K tile: A-operand rows of S^T,
+  // keys 16 t + l16 at chunk 4 kk + grp (+512 kk); transpose-read sources of K^T,
+  // keys 16 t + 4 grp + l16 / 4, columns 16 n + 4 (l16 % 4) (+256 n).
   int krow[2], trow[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    krow[t] = rho16(t * 16 + l16);
-    trow[t] = rho16(t * 16 + grp * 4 + (l16 >> 2)) * PS + (l16 & 3) * 4;
+    krow[t] = 8 * line_slot<D>(t * 16 + l16, grp);
+    trow[t] = 8 * line_slot<D>(t * 16 + grp * 4 + (l16 >> 2), (l16 & 3) >> 1) + 4 * (l16 & 1);
   }
-  // Key of accumulator row r of key tile t: u0 + 16 t + 2 r + goff.
-  const int goff = 8 * (grp & 1) + (grp >> 1);
+  // Key of accumulator row r of key tile t: u0 + 16 t + r + goff.
+  const int goff = 4 * grp;
 
   auto dma_kv = [&](int j, __bf16* kn, __bf16* vn) {
-    dma_pad<kQBN, D, kQThreads>(kr_, kv_row, j * kQBN, kn, wave, lane);
-    dma_xor<kQBN, D, kQThreads, true>(vr_, kv_row, j * kQBN, vn, wave, lane);
+    dma_lines<D, kQThreads>(kr_, kv_row, j * kQBN, kn, wave, lane);
+    dma_xor<kQBN, D, kQThreads>(vr_, kv_row, j * kQBN, vn, wave, lane);
   };
 
   auto tile = [&](int j, const __bf16* kt, const __bf16* vt, __bf16* kn, __bf16* vn) {
@@ -636,7 +620,7 @@ __global__ __launch_bounds__((QCfg<D, PACKED>::NT), (QCfg<D, PACKED>::NW == 4 ? 
     for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const bf16x8 ka = *(const bf16x8*)(kt + krow[t] * PS + kk * 32 + grp * 8);
+        const bf16x8 ka = *(const bf16x8*)(kt + krow[t] + kk * 512);
         const bf16x8 va = *(const bf16x8*)(vt + xoff<D>(t * 16 + l16, kk * 32 + grp * 8));
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
@@ -663,7 +647,7 @@ __global__ __launch_bounds__((QCfg<D, PACKED>::NT), (QCfg<D, PACKED>::NW == 4 ? 
         for (int x = 0; x < 2; ++x)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int u = u0 + 16 * t + 2 * r + goff;
+            const int u = u0 + 16 * t + r + goff;
             if (u < kv_lo[x] || u >= kv_lim[x]) s[t][x][r] = 0.0f;
           }
     }
@@ -679,7 +663,7 @@ __global__ __launch_bounds__((QCfg<D, PACKED>::NT), (QCfg<D, PACKED>::NW == 4 ? 
     // dQ^T += K^T dS^T per 16-row head-dim tile; K^T read transposed.
 #pragma unroll
     for (int n = 0; n < NDT; ++n) {
-      const bf16x8 kta = cat(tr_read(kt + trow[0] + n * 16), tr_read(kt + trow[1] + n * 16));
+      const bf16x8 kta = cat(tr_read(kt + trow[0] + n * 256), tr_read(kt + trow[1] + n * 256));
 #pragma unroll
       for (int x = 0; x < 2; ++x)
         dq_t[n][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kta, dsb[x], dq_t[n][x], 0, 0, 0);
