@@ -90,8 +90,8 @@ def parse():
     ap.add_argument("--aux-shape", default=None, choices=sorted(AUX_SHAPES),
                     help="with --aux: only this shape (one shape per counter run)")
     ap.add_argument("--sq-summary", metavar="DIR", default=None,
-                    help="print the markdown summary of the three SQ-counter --pmc runs under "
-                         "DIR (cnt_1/, cnt_2/, cnt_3/) and exit")
+                    help="print the markdown summary of the four SQ-counter --pmc runs under "
+                         "DIR (cnt_1/ .. cnt_4/) and exit")
     ap.add_argument("--trace-summary", metavar="DIR", default=None,
                     help="print the markdown summary of the rocprofv3 --kernel-trace --stats run "
                          "under DIR (run_kernel_stats.csv, and the bench line in DIR.log) and exit")

@@ -406,14 +406,19 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     }
     if (__builtin_expect(need_mask, 0)) {  // rare: keep it a branch
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+      for (int x = 0; x < 2; ++x) {
+        // packed: row c is kept iff lo_c <= c < hi_c, one unsigned compare of c - lo_c
+        // with the interval's width (c < lo_c wraps to a large value)
+        const uint32_t width = (uint32_t)max(hi_c[x] - lo_c[x], 0);
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+        for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int c = 16 * hf + r;
-            if (c < lo_c[x] || (PACKED && c >= hi_c[x])) s[hf][x][r] = 0.0f;
+            const bool drop = PACKED ? (uint32_t)(c - lo_c[x]) >= width : c < lo_c[x];
+            if (drop) s[hf][x][r] = 0.0f;
           }
+      }
     }
     bf16x8 pb[2], dsb[2];  // [key tile]; slot 4 hf + r
 #pragma unroll
@@ -642,14 +647,17 @@ __global__ __launch_bounds__((QCfg<D, PACKED>::NT), (QCfg<D, PACKED>::NW == 4 ? 
           s[t][x][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][x][r], a.scale_log2, -lse2[x]));
     if (__builtin_expect(need_mask, 0)) {  // rare: keep it a branch
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int x = 0; x < 2; ++x) {
+        // key u = u0 + 16 t + r + goff is kept iff kv_lo <= u < kv_lim: one unsigned
+        // compare of u - kv_lo with the interval's width
+        const int base = u0 + goff - kv_lo[x];
+        const uint32_t width = (uint32_t)max(kv_lim[x] - kv_lo[x], 0);
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int u = u0 + 16 * t + r + goff;
-            if (u < kv_lo[x] || u >= kv_lim[x]) s[t][x][r] = 0.0f;
-          }
+          for (int r = 0; r < 4; ++r)
+            if ((uint32_t)(base + 16 * t + r) >= width) s[t][x][r] = 0.0f;
+      }
     }
     bf16x8 dsb[2];  // [query half]; slot 4 t + r holds logical key 16 t + 4 grp + r
 #pragma unroll

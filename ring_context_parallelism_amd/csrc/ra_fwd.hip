@@ -392,15 +392,20 @@ __global__ __launch_bounds__((Bf16Cfg<D, PK>::NT), (Bf16Cfg<D, PK>::NW == 8 ? 1 
 
     const int u0 = j * BN;
     if (__builtin_expect(u0 < full_lo || u0 + BN > n_full, 0)) {  // rare: keep it a branch
+      // Key u = u0 + 16 t + 4 grp + r is visible to row x iff kv_lo <= u < kv_lim: one
+      // unsigned compare of u - kv_lo with the interval's width (u < kv_lo wraps to a
+      // large value).  Two signed compares per key left 64 lane masks live at once,
+      // which the compiler spilled to VGPR lanes.
 #pragma unroll
-      for (int t = 0; t < NKT; ++t)
+      for (int x = 0; x < 2; ++x) {
+        const int base = u0 + grp * 4 - kv_lo[x];
+        const uint32_t width = (uint32_t)max(kv_lim[x] - kv_lo[x], 0);
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+        for (int t = 0; t < NKT; ++t)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int u = u0 + t * 16 + grp * 4 + r;
-            if (u < kv_lo[x] || u >= kv_lim[x]) s[t][x][r] = kNegInf;
-          }
+          for (int r = 0; r < 4; ++r)
+            if ((uint32_t)(base + t * 16 + r) >= width) s[t][x][r] = kNegInf;
+      }
     }
 
     bf16x8 pb[2][NC];
