@@ -20,8 +20,9 @@
 //    them in step.
 //
 //  * dQ kernel -- the forward's shape: one workgroup = 8 waves = 256 query rows of
-//    one (batch, query head), KV tiles of 32 keys streamed through double-buffered
-//    LDS (each tile serves all 256 rows).  Scores are computed transposed,
+//    one (batch, query head) (4 waves = 128 rows with packed documents at D = 128),
+//    KV tiles of 32 keys streamed through double-buffered LDS (each tile serves all
+//    of the workgroup's rows).  Scores are computed transposed,
 //    S^T = K Q^T, on 16x16x32 MFMA tiles, so every lane holds two query rows; the
 //    dP^T accumulators start at -delta, and dS^T = P^T o (dP^T - delta) feeds
 //    dQ^T += K^T dS^T from registers, with K^T read by LDS transpose loads.
@@ -144,7 +145,6 @@ __device__ inline void dma_xor(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, in
 constexpr int kKvThreads = 256;  // 4 waves, each 32 keys
 constexpr int kKvBN = 128;       // keys per workgroup
 constexpr int kKvBQ = 32;        // query rows per iteration
-
 
 // PACKED: packed documents (a.seg != nullptr), a separate instantiation.
 //
