@@ -42,11 +42,18 @@ constexpr int kBM = 32 * kWaves;
 // than 4 waves on dense sequences; with packed documents the 4-wave workgroup is
 // faster (fewer workgroups straddle a document boundary, whose rows then see
 // disjoint key ranges), and at D = 32 it is faster too.
-template <int D, bool PK>
+//
+// HG query heads of one GQA group share a workgroup (HG = 4 at D = 128 when the group
+// allows it): 64 rows of each of 4 heads instead of 256 rows of one.  Each K/V tile
+// still serves 256 query rows, but the workgroup's causal diagonal is 4x narrower, so
+// fewer of its MFMAs fall above the diagonal and fewer of its tiles need a mask.
+template <int D, bool PK, int HG = 1>
 struct Bf16Cfg {
   static constexpr int NW = (D == 128 && !PK) ? 8 : 4;
   static constexpr int NT = 64 * NW;  // threads
-  static constexpr int BM = 32 * NW;  // query rows
+  static constexpr int WPH = NW / HG;  // waves per query head
+  static constexpr int BM = 32 * WPH;  // query rows per head
+  static_assert(NW % HG == 0, "whole waves per head");
 };
 
 // Max and sum over lanes l and l ^ 32 (the two halves of a wave).  permlane32_swap
@@ -283,11 +290,12 @@ __device__ inline void fwd_epilogue16(const FwdArgs& a, int b, int h, int tq, in
   if (grp == 0) a.lse_out[row] = lse_new;
 }
 
-template <int D, int BN, bool PK>
-__global__ __launch_bounds__((Bf16Cfg<D, PK>::NT), (Bf16Cfg<D, PK>::NW == 8 ? 1 : 2)) void fwd_bf16_kernel(
+template <int D, int BN, bool PK, int HG>
+__global__ __launch_bounds__((Bf16Cfg<D, PK, HG>::NT), (Bf16Cfg<D, PK, HG>::NW == 8 ? 1 : 2)) void fwd_bf16_kernel(
     FwdArgs a) {
-  constexpr int kBM = Bf16Cfg<D, PK>::BM;
-  constexpr int NT = Bf16Cfg<D, PK>::NT;
+  constexpr int kBM = Bf16Cfg<D, PK, HG>::BM;
+  constexpr int NT = Bf16Cfg<D, PK, HG>::NT;
+  constexpr int WPH = Bf16Cfg<D, PK, HG>::WPH;
   constexpr int NKK = D / 32;   // 32-wide head-dim steps of the QK^T contraction
   constexpr int NDT = D / 16;   // 16-row head-dim tiles of O^T
   constexpr int NKT = BN / 16;  // 16-key tiles per KV tile
@@ -305,12 +313,15 @@ __global__ __launch_bounds__((Bf16Cfg<D, PK>::NT), (Bf16Cfg<D, PK>::NW == 8 ? 1 
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int qi = logical % a.n_qtiles;
-  const int bh = logical / a.n_qtiles;
-  const int h = bh % a.Hq, b = bh / a.Hq;
+  const int bh = logical / a.n_qtiles;  // (batch, group of HG query heads)
+  const int hgn = a.Hq / HG;
+  const int h0 = (bh % hgn) * HG, b = bh / hgn;
+  const int h = h0 + wave / WPH;        // this wave's query head
   const int qt = a.n_qtiles - 1 - qi;  // heaviest (latest) query tiles first
   const int t0 = qt * kBM;
-  const int tq[2] = {t0 + wave * 32 + l16, t0 + wave * 32 + 16 + l16};
-  const int g = h / a.group;
+  const int wr = (wave % WPH) * 32;     // this wave's rows within the head's tile
+  const int tq[2] = {t0 + wr + l16, t0 + wr + 16 + l16};
+  const int g = h0 / a.group;           // HG divides the group: one KV head
 
   const __bf16* qb = (const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
   const __bf16* kb = (const __bf16*)a.k + (int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh;
@@ -652,26 +663,35 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 }
 
 template <typename K>
-hipError_t launch_grid(K kernel, const FwdArgs& a, int threads, hipStream_t s) {
-  const int64_t nblk = (int64_t)a.B * a.Hq * a.n_qtiles;
+hipError_t launch_grid(K kernel, const FwdArgs& a, int threads, hipStream_t s, int hg = 1) {
+  const int64_t nblk = (int64_t)a.B * (a.Hq / hg) * a.n_qtiles;
   hipLaunchKernelGGL(kernel, dim3((unsigned)nblk), dim3(threads), 0, s, a);
   return hipGetLastError();
 }
 
+// Query heads per bf16 workgroup: 4 at D = 128 on dense sequences when the GQA group
+// is a multiple of 4, else 1.
+int fwd_heads_per_wg(int dtype, int D, bool packed, int group) {
+  return (dtype == RA_BF16 && D == 128 && !packed && group % 4 == 0) ? 4 : 1;
+}
+
 }  // namespace
 
-int fwd_block_m(int dtype, int D, bool packed) {
+int fwd_block_m(int dtype, int D, bool packed, int group) {
   if (dtype != RA_BF16) return kBM;
   if (packed) return D == 128 ? Bf16Cfg<128, true>::BM : (D == 64 ? Bf16Cfg<64, true>::BM : Bf16Cfg<32, true>::BM);
+  if (fwd_heads_per_wg(dtype, D, packed, group) == 4) return Bf16Cfg<128, false, 4>::BM;
   return D == 128 ? Bf16Cfg<128, false>::BM : (D == 64 ? Bf16Cfg<64, false>::BM : Bf16Cfg<32, false>::BM);
 }
 
 template <bool PK>
 hipError_t launch_fwd_t(int dtype, int D, const FwdArgs& a, hipStream_t s) {
   if (dtype == RA_BF16) {
-    if (D == 128) return launch_grid(fwd_bf16_kernel<128, 64, PK>, a, Bf16Cfg<128, PK>::NT, s);
-    if (D == 64) return launch_grid(fwd_bf16_kernel<64, 64, PK>, a, Bf16Cfg<64, PK>::NT, s);
-    if (D == 32) return launch_grid(fwd_bf16_kernel<32, 64, PK>, a, Bf16Cfg<32, PK>::NT, s);
+    if (fwd_heads_per_wg(dtype, D, PK, a.group) == 4)
+      return launch_grid(fwd_bf16_kernel<128, 64, false, 4>, a, Bf16Cfg<128, false, 4>::NT, s, 4);
+    if (D == 128) return launch_grid(fwd_bf16_kernel<128, 64, PK, 1>, a, Bf16Cfg<128, PK>::NT, s);
+    if (D == 64) return launch_grid(fwd_bf16_kernel<64, 64, PK, 1>, a, Bf16Cfg<64, PK>::NT, s);
+    if (D == 32) return launch_grid(fwd_bf16_kernel<32, 64, PK, 1>, a, Bf16Cfg<32, PK>::NT, s);
   } else {
     if (D == 128) return launch_grid(fwd_f32_kernel<128, 32, PK>, a, kThreads, s);
     if (D == 64) return launch_grid(fwd_f32_kernel<64, 64, PK>, a, kThreads, s);

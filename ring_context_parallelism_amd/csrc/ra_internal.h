@@ -197,7 +197,7 @@ struct BwdArgs {
 hipError_t launch_fwd(int dtype, int D, const FwdArgs& a, hipStream_t s);
 // which: 1 = dK/dV kernel, 2 = dQ kernel, 3 = both.
 hipError_t launch_bwd(int dtype, int D, const BwdArgs& a, int which, hipStream_t s);
-int fwd_block_m(int dtype, int D, bool packed);
+int fwd_block_m(int dtype, int D, bool packed, int group);
 int bwd_block_n(int dtype, int D);
 hipError_t launch_lse_merge(int64_t rows, int32_t d, float* o_acc, float* lse_acc,
                             const float* o_part, const float* lse_part, hipStream_t s);

@@ -2,8 +2,8 @@
 
 Chunks of 1, 2, 3, 33, 65 and 66 tokens (a tile that is mostly ragged tail), zigzag
 sub-blocks of a single token, the striped layout with one token per chunk, p = 1,
-batch and head counts of 1 and 3, every rank's share, forward (bf16 and fp32) and
-backward, dense and packed.
+batch and head counts of 1 and 3, GQA groups of 4 and 8 (several query heads share a
+workgroup), every rank's share, forward (bf16 and fp32) and backward, dense and packed.
 """
 import numpy as np
 import pytest
@@ -31,6 +31,8 @@ CASES = [
     _wl("bf16", 64, 64, "striped", 3, 99, True, 1, 2, 2, True),          # L = 33
     _wl("bf16", 128, 128, "zigzag", 2, 132, True, 1, 2, 1, True),        # L = 66
     _wl("bf16", 128, 128, "contiguous", 1, 65, True, 1, 1, 1, True),     # p = 1, L = 65
+    _wl("bf16", 128, 128, "contiguous", 2, 6, True, 2, 8, 2, True),      # L = 3, GQA group 4
+    _wl("bf16", 128, 128, "zigzag", 2, 260, True, 1, 8, 1, True),        # L = 130, GQA group 8
     _wl("f32", 64, 64, "contiguous", 4, 4, True, 1, 1, 1, False),
     _wl("f32", 128, 128, "zigzag", 2, 4, True, 2, 2, 1, False),
     _wl("f32", 32, 24, "striped", 8, 8, False, 1, 3, 3, False),
