@@ -458,21 +458,32 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   // Store or add into dK and dV; accumulator row r of head-dim tile n is
-  // d = 16 n + 4 grp + r of this lane's key.
+  // d = 16 n + 4 grp + r of this lane's key.  When adding, a key's old values are all
+  // loaded before its first store: dk and dv may alias for all the compiler knows,
+  // so a load behind a store would wait for it.
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     if (!key_ok[x]) continue;
     const int64_t grow = (((int64_t)b * a.Hkv + g) * L + key[x]) * D;
+    f32x4* pk = (f32x4*)(a.dk + grow + grp * 4);
+    f32x4* pv = (f32x4*)(a.dv + grow + grp * 4);
+    if (a.write) {
 #pragma unroll
-    for (int n = 0; n < NDT; ++n) {
-      f32x4* pk = (f32x4*)(a.dk + grow + n * 16 + grp * 4);
-      f32x4* pv = (f32x4*)(a.dv + grow + n * 16 + grp * 4);
-      if (a.write) {
-        *pk = dk_t[n][x] * a.scale;
-        *pv = dv_t[n][x];
-      } else {
-        *pk = *pk + dk_t[n][x] * a.scale;
-        *pv = *pv + dv_t[n][x];
+      for (int n = 0; n < NDT; ++n) {
+        pk[4 * n] = dk_t[n][x] * a.scale;
+        pv[4 * n] = dv_t[n][x];
+      }
+    } else {
+      f32x4 ok[NDT], ov[NDT];
+#pragma unroll
+      for (int n = 0; n < NDT; ++n) {
+        ok[n] = pk[4 * n];
+        ov[n] = pv[4 * n];
+      }
+#pragma unroll
+      for (int n = 0; n < NDT; ++n) {
+        pk[4 * n] = ok[n] + dk_t[n][x] * a.scale;
+        pv[4 * n] = ov[n] + dv_t[n][x];
       }
     }
   }
@@ -686,19 +697,33 @@ __global__ __launch_bounds__((QCfg<D, PACKED>::NT), (QCfg<D, PACKED>::NW == 4 ? 
 
   // dQ[q][d] (+)= scale * dQ^T[d][q]; accumulator row r of tile n is d = 16 n + 4 grp + r.
   // A row that sees no key of this chunk adds nothing, or stores zeros in write mode.
+  // When adding, both rows' old values are loaded before the first store (a load
+  // behind a store to a possibly aliasing row would wait for it).
   if (n_tiles > j0 || a.write) {
+    f32x4* p[2];
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      if (tq[x] >= L) continue;
-      float* dqr = a.dq + (((int64_t)b * a.Hq + h) * L + tq[x]) * D;
+    for (int x = 0; x < 2; ++x)
+      p[x] = (f32x4*)(a.dq + (((int64_t)b * a.Hq + h) * L + min(tq[x], L - 1)) * D + grp * 4);
+    if (a.write) {
 #pragma unroll
-      for (int n = 0; n < NDT; ++n) {
-        f32x4* p = (f32x4*)(dqr + n * 16 + grp * 4);
-        if (a.write) {
-          *p = dq_t[n][x] * a.scale;
-        } else {
-          *p = *p + dq_t[n][x] * a.scale;
-        }
+      for (int x = 0; x < 2; ++x) {
+        if (tq[x] >= L) continue;
+#pragma unroll
+        for (int n = 0; n < NDT; ++n) p[x][4 * n] = dq_t[n][x] * a.scale;
+      }
+    } else {
+      f32x4 old[2][NDT];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        if (tq[x] >= L) continue;
+#pragma unroll
+        for (int n = 0; n < NDT; ++n) old[x][n] = p[x][4 * n];
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        if (tq[x] >= L) continue;
+#pragma unroll
+        for (int n = 0; n < NDT; ++n) p[x][4 * n] = old[x][n] + dq_t[n][x] * a.scale;
       }
     }
   }

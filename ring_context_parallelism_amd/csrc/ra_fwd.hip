@@ -237,57 +237,79 @@ __device__ inline float quad_sum(float x) {
   return pair_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
-// Epilogue of one query row in the 16x16 layout: o[dt] holds O^T[d][q] for
-// d = 16 dt + 4 grp + r.
+// Epilogue of the lane's two query rows in the 16x16 layout: o[dt][x] holds O^T[d][q]
+// for d = 16 dt + 4 grp + r.  Every load (the accumulator rows and their LSE) is
+// issued before the first store: the output may alias the accumulator, so a load
+// behind a store would have to wait for it.
 template <int D>
-__device__ inline void fwd_epilogue16(const FwdArgs& a, int b, int h, int tq, int grp, float m,
-                                      float l, const f32x4 (&o)[D / 16]) {
+__device__ inline void fwd_epilogue16(const FwdArgs& a, int b, int h, const int (&tq)[2], int grp,
+                                      const float (&m)[2], const float (&l)[2],
+                                      const f32x4 (&o)[D / 16][2]) {
+  constexpr int NDT = D / 16;
   const int L = a.map.L;
-  const float l_tot = quad_sum(l);
-  const bool live = l_tot > 0.0f;
-  const float lse_s = live ? (m * a.scale_log2 + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
-  const float inv_l = live ? 1.0f / l_tot : 0.0f;
-  if (tq >= L) return;
-  const int64_t row = ((int64_t)b * a.Hq + h) * L + tq;
-  float w_acc = 0.0f, w_s = inv_l, lse_new = lse_s;
-  if (a.acc_in != nullptr) {
-    const float lse_a = a.lse_in[row];
-    if (!live) {
-      w_acc = 1.0f;
-      w_s = 0.0f;
-      lse_new = lse_a;
-    } else if (lse_a == kNegInf) {
-      w_acc = 0.0f;
-    } else {
-      const float mx = fmaxf(lse_a, lse_s);
-      const float ea = __expf(lse_a - mx), es = __expf(lse_s - mx);
-      const float den = ea + es;
-      lse_new = mx + __logf(den);
-      w_acc = ea / den;
-      w_s = es / den * inv_l;
-    }
-  }
-  const float* acc = a.acc_in ? a.acc_in + row * D : nullptr;
-  char* obase = (char*)a.out;
-  const int64_t orow = (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)tq * a.o_st;
+  float lse_s[2], inv_l[2];
+  bool live[2], in[2];
+  int64_t row[2];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    const int d0 = dt * 16 + grp * 4;
-    f32x4 v = o[dt] * w_s;
-    if (acc != nullptr && w_acc != 0.0f) v += *(const f32x4*)(acc + d0) * w_acc;
-    if (a.out_f32) {
-      *(f32x4*)(obase + (orow + d0) * 4) = v;
-    } else {
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      bf16x4 w;
-      w[0] = (__bf16)v[0];
-      w[1] = (__bf16)v[1];
-      w[2] = (__bf16)v[2];
-      w[3] = (__bf16)v[3];
-      *(bf16x4*)(obase + (orow + d0) * 2) = w;
+  for (int x = 0; x < 2; ++x) {
+    const float l_tot = quad_sum(l[x]);
+    live[x] = l_tot > 0.0f;
+    lse_s[x] = live[x] ? (m[x] * a.scale_log2 + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
+    inv_l[x] = live[x] ? 1.0f / l_tot : 0.0f;
+    in[x] = tq[x] < L;
+    row[x] = ((int64_t)b * a.Hq + h) * L + min(tq[x], L - 1);
+  }
+  float lse_a[2] = {kNegInf, kNegInf};
+  f32x4 acc[2][NDT];
+  if (a.acc_in != nullptr) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      if (!in[x]) continue;
+      lse_a[x] = a.lse_in[row[x]];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        acc[x][dt] = *(const f32x4*)(a.acc_in + row[x] * D + dt * 16 + grp * 4);
     }
   }
-  if (grp == 0) a.lse_out[row] = lse_new;
+  char* obase = (char*)a.out;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    if (!in[x]) continue;
+    float w_acc = 0.0f, w_s = inv_l[x], lse_new = lse_s[x];
+    if (a.acc_in != nullptr) {
+      if (!live[x]) {
+        w_acc = 1.0f;
+        w_s = 0.0f;
+        lse_new = lse_a[x];
+      } else if (lse_a[x] != kNegInf) {
+        const float mx = fmaxf(lse_a[x], lse_s[x]);
+        const float ea = __expf(lse_a[x] - mx), es = __expf(lse_s[x] - mx);
+        const float den = ea + es;
+        lse_new = mx + __logf(den);
+        w_acc = ea / den;
+        w_s = es / den * inv_l[x];
+      }
+    }
+    const int64_t orow = (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)tq[x] * a.o_st;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int d0 = dt * 16 + grp * 4;
+      f32x4 v = o[dt][x] * w_s;
+      if (w_acc != 0.0f) v += acc[x][dt] * w_acc;
+      if (a.out_f32) {
+        *(f32x4*)(obase + (orow + d0) * 4) = v;
+      } else {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 w;
+        w[0] = (__bf16)v[0];
+        w[1] = (__bf16)v[1];
+        w[2] = (__bf16)v[2];
+        w[3] = (__bf16)v[3];
+        *(bf16x4*)(obase + (orow + d0) * 2) = w;
+      }
+    }
+    if (grp == 0) a.lse_out[row[x]] = lse_new;
+  }
 }
 
 template <int D, int BN, bool PK, int HG>
@@ -490,13 +512,7 @@ __global__ __launch_bounds__((Bf16Cfg<D, PK, HG>::NT), (Bf16Cfg<D, PK, HG>::NW =
     if (j + 1 < n_tiles) tile(j + 1, ks1, vs1, ks0, vs0);
   }
 
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    f32x4 ox[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) ox[dt] = o[dt][x];
-    fwd_epilogue16<D>(a, b, h, tq[x], grp, m[x], l[x], ox);
-  }
+  fwd_epilogue16<D>(a, b, h, tq, grp, m, l, o);
 }
 
 // ------------------------------------------------------------------------- fp32 path
