@@ -277,7 +277,7 @@ ra_status_t ra_block_attn_fwd(const ra_problem_t* prob, const void* q, int32_t q
     a.acc_in = o;
     a.lse_in = lse;
   }
-  hipError_t e = ra::launch_fwd(prob->dtype, (int)prob->head_dim_padded, a, stream);
+  hipError_t e = ra::launch_fwd(prob->dtype, (int)prob->head_dim_padded, (int)prob->head_dim, a, stream);
   if (e != hipSuccess) return hip_fail(e, "ra_block_attn_fwd launch");
   return ok();
 }
@@ -346,7 +346,7 @@ ra_status_t ra_ring_fwd(const ra_problem_t* prob, int32_t rank, const void* q,
       a.lse_in = lse;
     }
     a.lse_out = lse;
-    hipError_t e = ra::launch_fwd(prob->dtype, (int)prob->head_dim_padded, a, stream);
+    hipError_t e = ra::launch_fwd(prob->dtype, (int)prob->head_dim_padded, (int)prob->head_dim, a, stream);
     if (e != hipSuccess) return hip_fail(e, "ra_ring_fwd launch");
   }
   return ok();

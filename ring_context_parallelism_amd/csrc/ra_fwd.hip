@@ -517,7 +517,9 @@ __global__ __launch_bounds__((Bf16Cfg<D, PK, HG>::NT), (Bf16Cfg<D, PK, HG>::NW =
 
 // ------------------------------------------------------------------------- fp32 path
 
-template <int D, int BN, bool PK>
+// KP: column pairs of the QK^T contraction, D / 2, or 3 D / 8 when the true head dim
+// is at most 3 D / 4 (the remaining columns are zero padding).
+template <int D, int BN, bool PK, int KP>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
   constexpr int DP = D + 1;            // padded LDS row (conflict-free column reads)
   constexpr int NB = BN / 32;
@@ -544,9 +546,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
   const float* kb = (const float*)a.k + (int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh;
   const float* vb = (const float*)a.v + (int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh;
 
-  float qf[D / 2];
+  static_assert(KP == D / 2 || KP == 3 * D / 8, "full or three-quarter contraction");
+  float qf[KP];
 #pragma unroll
-  for (int kk = 0; kk < D / 2; ++kk) qf[kk] = tq < L ? qb[(int64_t)tq * a.q_st + kk * 2 + hh] : 0.0f;
+  for (int kk = 0; kk < KP; ++kk) qf[kk] = tq < L ? qb[(int64_t)tq * a.q_st + kk * 2 + hh] : 0.0f;
 
   // Visible keys of this row and of the workgroup, as in the bf16 kernel.
   int kv_lo = 0, kv_lim = L, j0 = 0, n_keys = L, full_lo = 0, n_full = L;
@@ -615,12 +618,14 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
     __syncthreads();
     if (j + 1 < n_tiles) load((j + 1) * BN);
 
+    // The contraction covers KP column pairs: the zero pad columns beyond the true
+    // head dim add nothing (at d = 24 stored as 32: 12 MFMAs instead of 16).
     f32x16 s[NB];
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       f32x16 acc = {};
 #pragma unroll
-      for (int kk = 0; kk < D / 2; ++kk) {
+      for (int kk = 0; kk < KP; ++kk) {
         const float kop = kf[buf][(blk * 32 + l32) * DP + kk * 2 + hh];
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kop, qf[kk], acc, 0, 0, 0);
       }
@@ -628,12 +633,14 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
     }
     const int u0 = j * BN;
     if (u0 < full_lo || u0 + BN > n_full) {
+      // visible iff kv_lo <= u < kv_lim: one unsigned compare of u - kv_lo
+      const uint32_t width = (uint32_t)max(kv_lim - kv_lo, 0);
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int u = u0 + blk * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-          if (u < kv_lo || u >= kv_lim) s[blk][i] = kNegInf;
+          if ((uint32_t)(u - kv_lo) >= width) s[blk][i] = kNegInf;
         }
     }
     float mx = s[0][0];
@@ -701,7 +708,7 @@ int fwd_block_m(int dtype, int D, bool packed, int group) {
 }
 
 template <bool PK>
-hipError_t launch_fwd_t(int dtype, int D, const FwdArgs& a, hipStream_t s) {
+hipError_t launch_fwd_t(int dtype, int D, int dk, const FwdArgs& a, hipStream_t s) {
   if (dtype == RA_BF16) {
     if (fwd_heads_per_wg(dtype, D, PK, a.group) == 4)
       return launch_grid(fwd_bf16_kernel<128, 64, false, 4>, a, Bf16Cfg<128, false, 4>::NT, s, 4);
@@ -709,15 +716,23 @@ hipError_t launch_fwd_t(int dtype, int D, const FwdArgs& a, hipStream_t s) {
     if (D == 64) return launch_grid(fwd_bf16_kernel<64, 64, PK, 1>, a, Bf16Cfg<64, PK>::NT, s);
     if (D == 32) return launch_grid(fwd_bf16_kernel<32, 64, PK, 1>, a, Bf16Cfg<32, PK>::NT, s);
   } else {
-    if (D == 128) return launch_grid(fwd_f32_kernel<128, 32, PK>, a, kThreads, s);
-    if (D == 64) return launch_grid(fwd_f32_kernel<64, 64, PK>, a, kThreads, s);
-    if (D == 32) return launch_grid(fwd_f32_kernel<32, 64, PK>, a, kThreads, s);
+    const bool part = 4 * dk <= 3 * D;  // true head dim within the first 3/4 of the columns
+    if (D == 128)
+      return part ? launch_grid(fwd_f32_kernel<128, 32, PK, 48>, a, kThreads, s)
+                  : launch_grid(fwd_f32_kernel<128, 32, PK, 64>, a, kThreads, s);
+    if (D == 64)
+      return part ? launch_grid(fwd_f32_kernel<64, 64, PK, 24>, a, kThreads, s)
+                  : launch_grid(fwd_f32_kernel<64, 64, PK, 32>, a, kThreads, s);
+    if (D == 32)
+      return part ? launch_grid(fwd_f32_kernel<32, 64, PK, 12>, a, kThreads, s)
+                  : launch_grid(fwd_f32_kernel<32, 64, PK, 16>, a, kThreads, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd(int dtype, int D, const FwdArgs& a, hipStream_t s) {
-  return a.seg != nullptr ? launch_fwd_t<true>(dtype, D, a, s) : launch_fwd_t<false>(dtype, D, a, s);
+hipError_t launch_fwd(int dtype, int D, int dk, const FwdArgs& a, hipStream_t s) {
+  return a.seg != nullptr ? launch_fwd_t<true>(dtype, D, dk, a, s)
+                          : launch_fwd_t<false>(dtype, D, dk, a, s);
 }
 
 }  // namespace ra

@@ -194,7 +194,8 @@ struct BwdArgs {
 };
 
 // Launchers (defined in the .hip files).  Return the hipError_t of the launch.
-hipError_t launch_fwd(int dtype, int D, const FwdArgs& a, hipStream_t s);
+// dk: the true head dim (the fp32 kernel skips the zero pad columns of QK^T).
+hipError_t launch_fwd(int dtype, int D, int dk, const FwdArgs& a, hipStream_t s);
 // which: 1 = dK/dV kernel, 2 = dQ kernel, 3 = both.
 hipError_t launch_bwd(int dtype, int D, const BwdArgs& a, int which, hipStream_t s);
 int fwd_block_m(int dtype, int D, bool packed, int group);
