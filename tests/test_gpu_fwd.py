@@ -224,3 +224,28 @@ def test_full_size_forward_sampled(w):
     if d < w.head_dim_padded:
         assert torch.all(out[..., d:] == 0)
     say(f"full-size forward {w.name}: {s}")
+
+
+@pytest.mark.timeout(600)
+def test_full_size_gqa_head_group_complete():
+    """The GQA striped share at full size, every row of heads 4..7 (one group of four
+    query heads on KV head 1, which share a forward workgroup) and of the last head,
+    element by element against the oracle's row-parallel driver."""
+    from oracle.rows import attention_fwd_rows, default_workers
+    dev = need_gpu()
+    w = WORKLOADS["gqa_striped"]
+    say("full-size GQA head group: generating inputs")
+    arrays = generate(w)
+    share = staging.stage(w, arrays, dev)
+    guard = Guarded()
+    out, lse = staging.ring_forward(share, w, alloc=guard)
+    torch.cuda.synchronize()
+    guard.check("full-size GQA head group")
+    heads = [4, 5, 6, 7, w.heads_q - 1]
+    say(f"full-size GQA head group: oracle on all {w.chunk_len} rows of heads {heads} "
+        f"({default_workers()} threads)")
+    O, LSE = attention_fwd_rows(arrays["q"], arrays["k"], arrays["v"], share.rows, w.causal,
+                                heads=heads)
+    s = assert_close(out[:, heads].float().cpu().numpy(), O, w.dtype, "GQA group O")
+    assert_lse(lse[:, heads].cpu().numpy(), LSE, "GQA group LSE")
+    say(f"full-size GQA head group: {s}")
