@@ -226,26 +226,38 @@ def test_full_size_forward_sampled(w):
     say(f"full-size forward {w.name}: {s}")
 
 
+COMPLETE = [  # (workload, heads compared on every row)
+    (WORKLOADS["gqa_striped"], [4, 5, 6, 7, 31]),  # one workgroup's group of 4 heads, and the last
+    (WORKLOADS["llama_share"], [0, 15]),
+    (WORKLOADS["tabular_rows"], [0, 3]),
+    (WORKLOADS["tabular_rows"].with_dtype("bf16"), [1]),
+]
+
+
 @pytest.mark.timeout(600)
-def test_full_size_gqa_head_group_complete():
-    """The GQA striped share at full size, every row of heads 4..7 (one group of four
-    query heads on KV head 1, which share a forward workgroup) and of the last head,
-    element by element against the oracle's row-parallel driver."""
+@pytest.mark.parametrize("w,heads", COMPLETE, ids=[f"{w.name}-{w.dtype}" for w, _ in COMPLETE])
+def test_full_size_forward_complete_heads(w, heads):
+    """A workload at full size with every row of some heads (every batch element)
+    compared element by element against the oracle's row-parallel driver; for the GQA
+    share, heads 4..7 are the four query heads on KV head 1 that share a forward
+    workgroup."""
     from oracle.rows import attention_fwd_rows, default_workers
     dev = need_gpu()
-    w = WORKLOADS["gqa_striped"]
-    say("full-size GQA head group: generating inputs")
+    say(f"full-size complete heads {w.name} {w.dtype}: generating inputs")
     arrays = generate(w)
     share = staging.stage(w, arrays, dev)
     guard = Guarded()
     out, lse = staging.ring_forward(share, w, alloc=guard)
     torch.cuda.synchronize()
-    guard.check("full-size GQA head group")
-    heads = [4, 5, 6, 7, w.heads_q - 1]
-    say(f"full-size GQA head group: oracle on all {w.chunk_len} rows of heads {heads} "
-        f"({default_workers()} threads)")
+    guard.check(f"full-size complete heads {w.name}")
+    d = w.head_dim
+    say(f"full-size complete heads {w.name}: oracle on all {w.chunk_len} rows of heads {heads} "
+        f"x {w.batch} batch ({default_workers()} threads)")
     O, LSE = attention_fwd_rows(arrays["q"], arrays["k"], arrays["v"], share.rows, w.causal,
                                 heads=heads)
-    s = assert_close(out[:, heads].float().cpu().numpy(), O, w.dtype, "GQA group O")
-    assert_lse(lse[:, heads].cpu().numpy(), LSE, "GQA group LSE")
-    say(f"full-size GQA head group: {s}")
+    got = out[:, heads].float().cpu().numpy()
+    s = assert_close(got[..., :d], O, w.dtype, f"{w.name} O")
+    assert_lse(lse[:, heads].cpu().numpy(), LSE, f"{w.name} LSE")
+    if d < w.head_dim_padded:
+        assert np.all(got[..., d:] == 0.0)
+    say(f"full-size complete heads {w.name}: {s}")
