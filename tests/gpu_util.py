@@ -56,8 +56,8 @@ def assert_lse(got, ref, what):
 
 
 class Guarded:
-    """Allocator of output buffers with a NaN guard tail (SURVEY's race-detection
-    canaries): every buffer starts as NaN, so an element a kernel fails to write
+    """Allocator of output buffers with a NaN guard tail (race-detection canaries):
+    every buffer starts as NaN, so an element a kernel fails to write
     stays NaN and fails the comparison, and `check()` asserts that no write went
     past the end of any buffer."""
 
