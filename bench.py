@@ -53,6 +53,8 @@ DEFAULT_WORKLOAD = "zigzag_fwdbwd"
 # The forward-only workloads the default run also times (each as one object of the
 # line's "configs" list), in the order of their sizes.
 OTHER_CONFIGS = ("tiny_fp32", "llama_share", "gqa_striped", "tabular_rows", "tabular_rows_bf16")
+# The packed-document share (forward and backward), reported beside them.
+PACKED_CONFIG = "packed_fwdbwd"
 
 KERNELS = {
     "fwd_kernel": ("fwd_bf16_kernel", ("ra_fwd.hip", "ra_internal.h")),
@@ -732,6 +734,116 @@ def time_fwd_steps(ra, prob, w, share, steps, ws, stream, reps):
     return [np.array([e[i].elapsed_time(e[i + 1]) for e in ev[1:]]) for i in range(n)]
 
 
+def packed_config(name, reps, stream):
+    """The packed-document share: ra_ring_fwd and ra_ring_bwd timed with HIP events over
+    `reps` passes after the default warmup, with FLOP counted inside documents only;
+    each live forward step timed on its own; and O, LSE and dQ on sampled rows and heads
+    against the oracle (a row's dQ depends on that row alone)."""
+    import numpy as np
+    import torch
+
+    from oracle.rows import attention_bwd_rows, attention_fwd_rows
+    from ring_context_parallelism_amd import ra, staging
+    from ring_context_parallelism_amd.workloads import WORKLOADS, generate
+    w = WORKLOADS[name]
+    print(f"[bench] config {name}: generating inputs", file=sys.stderr, flush=True)
+    arrays = generate(w)
+    bounds = arrays["bounds"]
+    dev = torch.device("cuda:0")
+    share = staging.stage(w, arrays, dev)
+    prob = share.prob
+    steps = step_flops(w, prob, ra, bounds)
+    L, D, d = w.chunk_len, w.head_dim_padded, w.head_dim
+    f32 = torch.float32
+    out = torch.empty((w.batch, w.heads_q, L, D), dtype=staging.torch_dtype(w), device=dev)
+    lse = torch.empty((w.batch, w.heads_q, L), dtype=f32, device=dev)
+    ws = torch.empty(ra.ra_ring_workspace_size(prob) // 4, dtype=f32, device=dev)
+    dq = torch.empty((w.batch, w.heads_q, L, D), dtype=f32, device=dev)
+    dks = [torch.empty((w.batch, w.heads_kv, L, D), dtype=f32, device=dev) for _ in range(w.world)]
+    dvs = [torch.empty_like(dks[0]) for _ in range(w.world)]
+    wsb = torch.empty(ra.ra_ring_bwd_workspace_size(prob) // 4, dtype=f32, device=dev)
+
+    def fwd():
+        ra.ra_ring_fwd(prob, w.rank, share.q, share.k_chunks, share.v_chunks, out, lse, ws,
+                       stream=stream)
+
+    def bwd():
+        ra.ra_ring_bwd(prob, w.rank, share.q, share.k_chunks, share.v_chunks, out, share.do, lse,
+                       dq, dks, dvs, wsb, stream=stream)
+
+    def run():
+        fwd()
+        bwd()
+
+    _warm(run, stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for e in ev:
+        e[0].record(stream)
+        fwd()
+        e[1].record(stream)
+        bwd()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    fms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    bms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    fflop = sum(st["fwd_flop"] for st in steps)
+    bflop = sum(st["bwd_flop"] for st in steps)
+    peak = BF16_PEAK_TFLOPS
+    ftf = fflop / (float(np.mean(fms)) * 1e-3) / 1e12
+    btf = bflop / (float(np.mean(bms)) * 1e-3) / 1e12
+    step_tf = (fflop + bflop) / (float(np.mean(fms + bms)) * 1e-3) / 1e12
+    step_ms = time_fwd_steps(ra, prob, w, share, steps, ws, stream, max(3, reps))
+    per_step = [dict(step=st["step"], chunk=st["chunk"],
+                     visible_pairs_per_head=st["visible_pairs_per_head"],
+                     fwd_ms=float(np.mean(sm)), fwd_ms_median=float(np.median(sm)),
+                     fwd_pct_peak=100.0 * st["fwd_flop"] / (float(np.mean(sm)) * 1e-3) / 1e12 / peak)
+                for st, sm in zip(steps, step_ms)]
+    # parity on sampled rows (tile edges + random) of sampled heads
+    run()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed)
+    t_idx = np.unique(np.concatenate([
+        np.array([0, 1, 127, 128, L // 2, L - 129, L - 128, L - 1]),
+        rng.choice(L, size=48, replace=False)]))
+    heads = sorted({0, w.heads_q - 1, *rng.choice(w.heads_q, size=2, replace=False).tolist()})
+    rows = share.rows[t_idx]
+    O, LSE = attention_fwd_rows(arrays["q"], arrays["k"], arrays["v"], rows, w.causal,
+                                heads=heads, bounds=bounds)
+    dQ, _, _ = attention_bwd_rows(arrays["q"], arrays["k"], arrays["v"],
+                                  arrays["do"][:, heads][:, :, rows], rows, w.causal,
+                                  heads=heads, bounds=bounds)
+    ti = torch.from_numpy(t_idx).to(dev)
+    got = out[:, heads][:, :, ti].float().cpu().numpy()[..., :d]
+    gdq = dq[:, heads][:, :, ti].cpu().numpy()[..., :d]
+    lg = lse[:, heads][:, :, ti].cpu().numpy()
+    fin = np.isfinite(LSE)
+
+    def errs(a, b):
+        e = np.abs(a - b)
+        nb = np.linalg.norm(b)
+        return {"max_abs": float(e.max()), "mean_abs": float(e.mean()),
+                "rel_fro": float(np.linalg.norm(a - b) / nb) if nb > 0 else 0.0}
+
+    par = {"rows": int(t_idx.size), "heads": heads, "o": errs(got, O), "dq": errs(gdq, dQ),
+           "lse_max_abs": float(np.abs(lg[fin] - LSE[fin]).max()) if fin.any() else 0.0,
+           "lse_inf_rows_match": bool(np.array_equal(np.isneginf(lg), np.isneginf(LSE)))}
+    par["pass"] = bool(all(par[k]["max_abs"] <= 2e-2 and par[k]["mean_abs"] <= 2e-3
+                           and par[k]["rel_fro"] <= 1e-2 for k in ("o", "dq"))
+                       and par["lse_max_abs"] <= 1e-3 and par["lse_inf_rows_match"])
+    rec = {"workload": name, "dtype": w.dtype, "batch": w.batch, "heads_q": w.heads_q,
+           "heads_kv": w.heads_kv, "head_dim": w.head_dim, "seq_total": w.seq_total,
+           "world": w.world, "layout": w.layout, "rank": w.rank, "causal": w.causal,
+           "documents": int(bounds.shape[-1] - 1), "passes": "fwd+bwd", "reps": reps,
+           "fwd_ms": round(float(np.mean(fms)), 4), "bwd_ms": round(float(np.mean(bms)), 4),
+           "fwd_flop": fflop, "bwd_flop": bflop, "fwd_tflops": round(ftf, 3),
+           "bwd_tflops": round(btf, 3), "fwd_pct_peak": round(100.0 * ftf / peak, 2),
+           "bwd_pct_peak": round(100.0 * btf / peak, 2), "step_tflops": round(step_tf, 3),
+           "peak": peak, "per_step": per_step, "parity": par}
+    del share, arrays, out, lse, ws, dq, dks, dvs, wsb
+    torch.cuda.empty_cache()
+    return rec
+
+
 def _warm(fn, stream):
     """Untimed warmup: at least 2 calls and about WARM_SECONDS of work."""
     import torch
@@ -1044,6 +1156,7 @@ def main():
         torch.cuda.empty_cache()
         res["configs"] = [other_config(name, args.steps, stream)
                           for name in OTHER_CONFIGS]
+        res["configs"].append(packed_config(PACKED_CONFIG, args.steps, stream))
     print(json.dumps(res), flush=True)
 
 
