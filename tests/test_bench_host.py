@@ -160,3 +160,23 @@ def test_trace_summary_counts_the_timed_launches_only(tmp_path):
     assert abs(data["kernels"]["bwd_dkdv_kernel"]["median_ms"] - 10.0) < 1e-9
     pairs = 2 * (2147516416 + 2147483648) / 2 * 16 / 2
     assert abs(data["kernels"]["fwd_kernel"]["tflops"] - 512 * pairs / 10e-3 / 1e12) < 1e-6
+
+
+def test_rows_parity_handles_padding_rows():
+    """The packed share's row check: -inf LSE rows (padding) must match exactly, finite
+    rows are compared, and an error in O, dQ or one padding row fails it."""
+    rng = np.random.default_rng(3)
+    O = rng.standard_normal((1, 2, 10, 8))
+    dQ = rng.standard_normal((1, 2, 10, 8))
+    LSE = rng.standard_normal((1, 2, 10))
+    O[:, :, 7:] = 0.0
+    dQ[:, :, 7:] = 0.0
+    LSE[:, :, 7:] = -np.inf
+    res = bench.rows_parity(O.copy(), O, LSE.copy(), LSE, dQ.copy(), dQ)
+    assert res["pass"] and res["lse_inf_rows_match"] and res["lse_max_abs"] == 0.0
+    bad = LSE.copy()
+    bad[0, 1, 8] = 0.5  # a padding row that saw something
+    assert not bench.rows_parity(O, O, bad, LSE, dQ, dQ)["pass"]
+    assert not bench.rows_parity(O + 0.1, O, LSE, LSE, dQ, dQ)["pass"]
+    assert not bench.rows_parity(O, O, LSE, LSE, dQ + 0.1, dQ)["pass"]
+    assert bench.rows_parity(O, O, LSE + 5e-4, LSE)["pass"]  # forward only, LSE within 1e-3
