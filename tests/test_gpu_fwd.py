@@ -39,6 +39,8 @@ SMALL = [
     _wl("f32", 32, 24, "contiguous", 4, 1000, False, 2, 2, 2, dist="uniform", scale=1.0),
     _wl("f32", 128, 128, "striped", 2, 520, True, 1, 2, 1),
     _wl("f32", 64, 40, "zigzag", 2, 520, True, 1, 2, 2),
+    _wl("bf16", 128, 128, "contiguous", 2, 520, False, 2, 8, 2),  # 4 GQA heads per workgroup
+    _wl("f32", 128, 96, "striped", 2, 520, True, 1, 2, 1),       # fp32 QK^T over 3/4 of D
 ]
 
 
