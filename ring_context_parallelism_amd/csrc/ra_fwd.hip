@@ -9,8 +9,9 @@
 // which the epilogue either writes or LSE-merges into an accumulator.
 //
 // Work decomposition (gfx950, wave64):
-//  * one workgroup = 4 or 8 waves = BM = 128 or 256 query rows of one (batch,
-//    query head) (8 at head dim 128); each wave owns 32 query rows;
+//  * one workgroup = 4 or 8 waves = 128 or 256 query rows of one (batch, query
+//    head) (8 at head dim 128), or, with GQA groups of 4 or more at head dim 128, 64
+//    rows of each of 4 query heads that read one KV head; each wave owns 32 rows;
 //  * the KV chunk is streamed in tiles of BN keys through double-buffered LDS;
 //  * bf16: scores are computed transposed, S^T = K Q^T, with 16x16x32 MFMA tiles;
 //    every lane holds two query rows and a quarter of their keys, so the softmax
@@ -20,7 +21,8 @@
 //  * the reference max of the online softmax moves lazily: P is taken against the
 //    current reference, and only when a lane's partial row sum of a tile exceeds
 //    2^8 does the wave find the exact row max and rescale (so p <= 2^8 always);
-//  * fp32 problems use the fp32 32x32x2 MFMA with K and V row-major in LDS.
+//  * fp32 problems use the fp32 32x32x2 MFMA with K and V row-major in LDS; its QK^T
+//    contraction stops at the true head dim when that leaves a quarter of D as padding.
 #include "ra_internal.h"
 
 namespace ra {
