@@ -97,6 +97,8 @@ def parse():
     ap.add_argument("--trace-summary", metavar="DIR", default=None,
                     help="print the markdown summary of the rocprofv3 --kernel-trace --stats run "
                          "under DIR (run_kernel_stats.csv, and the bench line in DIR.log) and exit")
+    ap.add_argument("--aux-summary", metavar="FILE", default=None,
+                    help="print the markdown summary of a saved --aux JSON line and exit")
     ap.add_argument("--pmc-summary", metavar="DIR", default=None,
                     help="print the markdown traffic summary of the rocprofv3 --pmc runs under "
                          "DIR (pmc_fetch/, pmc_write/, pmc_copy_fetch/, pmc_copy_write/) and exit")
@@ -649,6 +651,32 @@ def copy_probe(nbytes):
     print(json.dumps({"copy_probe_bytes": nbytes}), flush=True)
 
 
+def aux_summary(path):
+    """Markdown table of a saved `bench.py --aux` line (the helpers' HIP-event timings)."""
+    rec = json.loads([ln for ln in open(path) if ln.strip().startswith("{")][-1])
+    lines = ["# HBM-bound helper kernels: standalone LSE merge and backward delta", "",
+             "Commands (one MI355X):", "", "```", "python3 <repo>/bench.py --aux > <out>/aux.json",
+             "python3 <repo>/bench.py --aux-summary <out>/aux.json", "```", "",
+             "Each kernel is launched 50 times back to back after one warm-up launch; HIP events "
+             "on the launch stream give the average duration.  Algorithmic bytes per row: the "
+             "merge reads both fp32 partials and both LSEs and writes the accumulator and its "
+             "LSE, (3 d + 3) x 4 B; delta reads O and dO in bf16 (2 d x 2 B) and writes 4 B.", "",
+             f"| kernel | shape | bytes per launch | ms | achieved (GB/s) | fraction of {HBM_PEAK_GBS:.0f} GB/s |",
+             "|---|---|---|---|---|---|"]
+    for k in rec["kernels"]:
+        lines.append(f"| `{k['kernel']}` | {k['shape']} | {k['bytes']} | {k['ms']} | {k['achieved']} | "
+                     f"{k['frac']} |")
+    c = rec.get("copy_reference")
+    if c:
+        lines += ["", f"Reference on the same box: a plain 1 GiB device-to-device copy through torch "
+                      f"moves {c['bytes']} bytes (read + write) in {c['ms']} ms = {c['achieved']} GB/s "
+                      f"({c['frac']} of {HBM_PEAK_GBS:.0f} GB/s).  The llama_share merge (203 MB) may "
+                      f"partly hit the 256 MB last-level cache on repeated launches; the zigzag_fwdbwd "
+                      f"shapes (0.5-1.6 GB) do not.  FETCH_SIZE / WRITE_SIZE counts for the zig-zag "
+                      f"shapes are in pmc_traffic_hbm_helpers.md."]
+    return "\n".join(lines)
+
+
 def aux_bench(reps=50, only=None):
     """The HBM-bound helpers against the 8 TB/s roofline, at the llama_share and
     zigzag_fwdbwd shapes: the standalone LSE merge (rows x d fp32 partials) and the
@@ -960,6 +988,9 @@ def main():
         print("[bench] source hashes " + json.dumps({k: source_hash(f) for k, (_, f) in KERNELS.items()}),
               file=sys.stderr, flush=True)
         aux_bench(only=args.aux_shape)
+        return
+    if args.aux_summary:
+        print(aux_summary(args.aux_summary))
         return
     if args.pmc_summary:
         print(pmc_summary(args.pmc_summary, args.workload))

@@ -180,3 +180,14 @@ def test_rows_parity_handles_padding_rows():
     assert not bench.rows_parity(O + 0.1, O, LSE, LSE, dQ, dQ)["pass"]
     assert not bench.rows_parity(O, O, LSE, LSE, dQ + 0.1, dQ)["pass"]
     assert bench.rows_parity(O, O, LSE + 5e-4, LSE)["pass"]  # forward only, LSE within 1e-3
+
+
+def test_aux_summary_renders_a_saved_line(tmp_path):
+    rec = {"kernels": [{"kernel": "lse_merge_kernel", "shape": "x: 10 rows x 8", "ms": 0.5,
+                        "bytes": 1000, "achieved": 2.0, "peak": 8000.0, "frac": 0.00025}],
+           "copy_reference": {"bytes": 2048, "ms": 0.1, "achieved": 20.5, "frac": 0.0026}}
+    f = tmp_path / "aux.json"
+    f.write_text("noise\n" + json.dumps(rec) + "\n")
+    md = bench.aux_summary(str(f))
+    assert "| `lse_merge_kernel` | x: 10 rows x 8 | 1000 | 0.5 | 2.0 | 0.00025 |" in md
+    assert "20.5 GB/s" in md
