@@ -10,7 +10,10 @@ rank 0, bf16 -- the only workload that exercises every step, forward and backwar
 
 Inputs are synthetic (seeded, see ring_context_parallelism_amd/workloads.py) and
 already resident in HBM when the timed region starts.  Timing uses HIP events on
-the stream the kernels are launched on.  Prints ONE JSON line.
+the stream the kernels are launched on.  Prints ONE JSON line: the headline share
+with its roofline, parity and the oracle's CPU rate, and (default run) every other
+workload -- the forward shares, and the packed-document share forward and backward --
+each timed with its own parity check.
 """
 from __future__ import annotations
 
