@@ -7,7 +7,10 @@
   rows that see nothing (0 and -inf), and RA_MERGE chains in ring order;
 * the standalone LSE merge against the oracle's merge, -inf rows included;
 * every workload at its full size through ra_ring_fwd (the launch configuration
-  the benchmark times), on sampled rows and heads the oracle computes one by one.
+  the benchmark times), on sampled rows and heads the oracle computes one by one,
+  and on every row of some heads (for GQA, one workgroup's group of four heads);
+* the rescaling path of the online softmax driven on most tiles (moving-max inputs),
+  and run-to-run determinism.
 """
 import numpy as np
 import pytest
