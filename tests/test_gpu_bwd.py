@@ -5,6 +5,7 @@
   dK, dV of every KV chunk -- element by element;
 * ra_block_attn_bwd accumulates (+=) and a step with no visible pair is a no-op;
 * ra_bwd_delta against the oracle's rowsum(dO * O);
+* a softmax scale set in the problem (not 1/sqrt(d)), forward and backward;
 * the forward+backward zigzag workload at full size: dQ of every row and dK, dV of
   every key for two heads, element by element, plus two identities that hold at
   any size over all heads, sum_j dV_j = sum_i dO_i and sum_j dK_j = 0 (per KV head).
@@ -16,7 +17,7 @@ import torch
 import oracle
 from ring_context_parallelism_amd import ra, staging
 from ring_context_parallelism_amd.workloads import WORKLOADS, Workload, generate
-from tests.gpu_util import Guarded, assert_close, need_gpu, say
+from tests.gpu_util import Guarded, assert_close, assert_lse, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -245,3 +246,39 @@ def test_split_entry_points_match_combined():
     torch.cuda.synchronize()
     for t in (dq, dk, dv):
         assert torch.count_nonzero(torch.nan_to_num(t, nan=1.0)).item() == 0
+
+
+@pytest.mark.parametrize("dtype,scale", [("bf16", 0.21), ("f32", 0.6)])
+def test_custom_softmax_scale(dtype, scale):
+    """A softmax scale set in the problem instead of 1/sqrt(head_dim): the forward (and,
+    in bf16, the backward) of every rank's share against the oracle at that scale."""
+    dev = need_gpu()
+    w = Workload(f"scale_{dtype}", 210, dtype, 1, 4, 2, 96, 128, 520, 2, "zigzag", 0, True,
+                 "normal", 0.5, backward=dtype == "bf16")
+    arrays = generate(w)
+    d = w.head_dim
+    for r in range(w.world):
+        say(f"custom scale {scale} {dtype} rank {r}")
+        share = staging.stage(w, arrays, dev, rank=r)
+        share.prob.scale = scale
+        guard = Guarded()
+        out, lse = staging.ring_forward(share, w, rank=r, alloc=guard)
+        torch.cuda.synchronize()
+        rows = oracle.positions(w.layout, w.seq_total, w.world, r)
+        O, LSE = oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, True,
+                                      scale=scale)
+        assert_close(_np(out)[..., :d], O, dtype, f"O scale {scale} rank {r}")
+        assert_lse(_np(lse), LSE, f"LSE scale {scale} rank {r}")
+        if dtype != "bf16":
+            guard.check(f"custom scale fwd rank {r}")
+            continue
+        dq, dks, dvs = staging.ring_backward(share, w, out, lse, rank=r, alloc=guard)
+        torch.cuda.synchronize()
+        guard.check(f"custom scale fwd+bwd rank {r}")
+        dQ, dK, dV = oracle.attention_bwd(arrays["q"], arrays["k"], arrays["v"],
+                                          arrays["do"][:, :, rows], rows, True, scale=scale)
+        assert_close(_np(dq)[..., :d], dQ, "bf16", f"dQ scale {scale} rank {r}")
+        for c in range(w.world):
+            pos = oracle.positions(w.layout, w.seq_total, w.world, c)
+            assert_close(_np(dks[c])[..., :d], dK[:, :, pos], "bf16", f"dK scale chunk {c}")
+            assert_close(_np(dvs[c])[..., :d], dV[:, :, pos], "bf16", f"dV scale chunk {c}")
