@@ -61,7 +61,7 @@ PACKED_CONFIG = "packed_fwdbwd"
 
 KERNELS = {
     "fwd_kernel": ("fwd_bf16_kernel", ("ra_fwd.hip", "ra_internal.h")),
-    "fwd_kernel_f32": ("fwd_f32_kernel", ("ra_fwd.hip", "ra_internal.h")),
+    "fwd_kernel_f32": ("fwd_f32_kernel", ("ra_fwd_f32.hip", "ra_internal.h")),
     "bwd_dkdv_kernel": ("bwd_dkdv_kernel", ("ra_bwd.hip", "ra_internal.h")),
     "bwd_dq_kernel": ("bwd_dq_kernel", ("ra_bwd.hip", "ra_internal.h")),
     "lse_merge_kernel": ("lse_merge_kernel", ("ra_misc.hip", "ra_internal.h")),
@@ -109,10 +109,15 @@ def parse():
 
 
 def source_hash(files):
+    """Hash of a kernel's source files and of the compiler flags they are built with
+    (a flag can change the code as much as the source)."""
+    from ring_context_parallelism_amd import build as _build
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
+        if f.endswith(".hip"):
+            h.update(" ".join(_build.FLAGS + _build.SOURCE_FLAGS.get(f, [])).encode())
     return h.hexdigest()[:16]
 
 

@@ -44,13 +44,6 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ inline int xcd_remap(int bid, int nblk) {
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int per = (nblk + 7) >> 3, rem = nblk & 7;
-  if (rem == 0 || xcd < rem) return xcd * per + slot;
-  return rem * per + (xcd - rem) * (per - 1) + slot;
-}
-
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }

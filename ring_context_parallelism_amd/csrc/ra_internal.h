@@ -103,6 +103,28 @@ __host__ __device__ inline void query_interval(const LayoutMap& m, int32_t cq, i
 }
 
 #if defined(__HIPCC__)
+// Workgroup id -> logical work item.  Workgroups are dispatched round-robin over the
+// 8 XCDs, so give every XCD one contiguous range of logical ids: the tiles that share
+// a head (and so its K/V or Q reads) then share that XCD's L2.
+__device__ inline int xcd_remap(int bid, int nblk) {
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int per = (nblk + 7) >> 3, rem = nblk & 7;
+  if (rem == 0 || xcd < rem) return xcd * per + slot;
+  return rem * per + (xcd - rem) * (per - 1) + slot;
+}
+
+// Max and sum over lanes l and l ^ 32 (the two halves of a wave).  permlane32_swap
+// returns (own, partner) in lanes < 32 and (partner, own) in lanes >= 32, so a max or
+// a sum of the pair needs no select.
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Workgroup-wide (min lo, max hi, max lo, min hi) of per-row intervals [lo, hi)
 // (packed documents): tiles from min lo to max hi hold every visible pair, and
 // [max lo, min hi) is visible to every row.  A lane holding several rows passes the
@@ -196,6 +218,10 @@ struct BwdArgs {
 // Launchers (defined in the .hip files).  Return the hipError_t of the launch.
 // dk: the true head dim (the fp32 kernel skips the zero pad columns of QK^T).
 hipError_t launch_fwd(int dtype, int D, int dk, const FwdArgs& a, hipStream_t s);
+// The fp32 forward (ra_fwd_f32.hip), which launch_fwd calls for fp32 problems; its
+// workgroups take kFwdF32BlockM query rows of one head.
+constexpr int kFwdF32BlockM = 128;
+hipError_t launch_fwd_f32(int D, int dk, bool packed, const FwdArgs& a, hipStream_t s);
 // which: 1 = dK/dV kernel, 2 = dQ kernel, 3 = both.
 hipError_t launch_bwd(int dtype, int D, const BwdArgs& a, int which, hipStream_t s);
 int fwd_block_m(int dtype, int D, bool packed, int group);

@@ -191,3 +191,15 @@ def test_aux_summary_renders_a_saved_line(tmp_path):
     md = bench.aux_summary(str(f))
     assert "| `lse_merge_kernel` | x: 10 rows x 8 | 1000 | 0.5 | 2.0 | 0.00025 |" in md
     assert "20.5 GB/s" in md
+
+
+def test_source_hash_covers_the_compiler_flags(monkeypatch):
+    from ring_context_parallelism_amd import build
+    files = bench.KERNELS["bwd_dq_kernel"][1]
+    before = bench.source_hash(files)
+    monkeypatch.setitem(build.SOURCE_FLAGS, "ra_bwd.hip", ["-mllvm", "-amdgpu-sched-strategy=ilp"])
+    changed = bench.source_hash(files)
+    assert changed != before
+    # a flag of another source leaves this kernel's hash alone
+    monkeypatch.setitem(build.SOURCE_FLAGS, "ra_fwd_f32.hip", ["-O2"])
+    assert bench.source_hash(files) == changed
