@@ -88,11 +88,69 @@ __host__ __device__ constexpr int pair_slot(int m, int c) {
   return 16 * ((COLS / 8) * (m >> 4) + (COLS / 16) * ((m >> 3) & 1) + (c >> 1)) +
          2 * ((m & 7) ^ ((m >> 3) & 1)) + (c & 1);
 }
+// The inverse: the row and chunk stored in a slot.
+template <int COLS>
+__host__ __device__ constexpr int pair_row(int slot) {
+  constexpr int CH = COLS / 8;
+  const int line = slot >> 4, o = (line % CH) / (CH / 2);
+  return 16 * (line / CH) + 8 * o + (((slot & 15) >> 1) ^ o);
+}
+template <int COLS>
+__host__ __device__ constexpr int pair_chunk(int slot) {
+  constexpr int CH = COLS / 8;
+  return 2 * ((slot >> 4) % CH % (CH / 2)) + (slot & 1);
+}
 // Element offsets in a pair tile: a row read 4 chunks on, a transpose read 2 chunks on.
 template <int COLS>
 constexpr int kPairRowStep = 8 * (pair_slot<COLS>(0, 4) - pair_slot<COLS>(0, 0));
 template <int COLS>
 constexpr int kPairTrStep = 8 * (pair_slot<COLS>(0, 2) - pair_slot<COLS>(0, 0));
+
+// Compile-time check of the claims above: the slots are a bijection onto the tile, the
+// inverse matches, each read steps by the compile-time offsets, and every row-read pass
+// (8 rows of one parity in one 16-row half, one chunk pair) and every transpose pass
+// (one octet, one chunk pair) covers 16 distinct bank groups.
+template <int COLS>
+constexpr bool pair_tile_ok() {
+  constexpr int CH = COLS / 8;
+  bool seen[32 * CH] = {};
+  for (int m = 0; m < 32; ++m)
+    for (int c = 0; c < CH; ++c) {
+      const int s = pair_slot<COLS>(m, c);
+      if (s < 0 || s >= 32 * CH || seen[s]) return false;
+      if (pair_row<COLS>(s) != m || pair_chunk<COLS>(s) != c) return false;
+      if (c >= 4 && 8 * pair_slot<COLS>(m, c) != 8 * pair_slot<COLS>(m, c - 4) + kPairRowStep<COLS>)
+        return false;
+      if (c >= 2 && 8 * pair_slot<COLS>(m, c) != 8 * pair_slot<COLS>(m, c - 2) + kPairTrStep<COLS>)
+        return false;
+      seen[s] = true;
+    }
+  for (int first = 0; first < 32; ++first) {  // row-read passes: rows first, first + 2, ...
+    if ((first & 15) >= 2) continue;
+    for (int c0 = 0; c0 < CH; c0 += 2) {
+      bool g[16] = {};
+      for (int i = 0; i < 8; ++i)
+        for (int b = 0; b < 2; ++b) {
+          const int grp = pair_slot<COLS>(first + 2 * i, c0 + b) & 15;
+          if (g[grp]) return false;
+          g[grp] = true;
+        }
+    }
+  }
+  for (int o = 0; o < 4; ++o)  // transpose passes
+    for (int c0 = 0; c0 < CH; c0 += 2) {
+      bool g[16] = {};
+      for (int r = 0; r < 8; ++r)
+        for (int b = 0; b < 2; ++b) {
+          const int grp = pair_slot<COLS>(8 * o + r, c0 + b) & 15;
+          if (g[grp]) return false;
+          g[grp] = true;
+        }
+    }
+  return true;
+}
+static_assert(pair_tile_ok<128>() && pair_tile_ok<64>() && pair_tile_ok<32>(),
+              "pair tile: bijection, inverse, offsets and one pass per read");
 
 // Swizzled tile (16-byte row reads only): XOR the chunk with the row's index among
 // the rows that share one 256-byte bank window, so 16 consecutive rows at one
@@ -121,10 +179,7 @@ __device__ inline void dma_pairs(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, 
     const int base = it * NT + wave * 64;
     if (SLOTS % NT != 0 && base >= SLOTS) break;  // wave-uniform
     const int slot = base + lane;
-    const int line = slot >> 4, grp16 = slot & 15;
-    const int o = (line % CH) / (CH / 2);            // octet parity
-    const int c = 2 * ((line % CH) % (CH / 2)) + (grp16 & 1);
-    const int m = 16 * (line / CH) + 8 * o + ((grp16 >> 1) ^ o);
+    const int m = pair_row<COLS>(slot), c = pair_chunk<COLS>(slot);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + base * 8), 16,
                                              (uint32_t)(r0 + m) * row_bytes + (uint32_t)c * 16u,
                                              0, 0, 0);
