@@ -81,9 +81,14 @@ struct Bf16Tile {
   static constexpr int RPW = 256 / (D * 2);         // rows per 256-byte bank window
 };
 
-// K tile: LDS serves 16 lanes x 16 bytes per clock from 64 four-byte banks, and the
-// 16-byte K reads of one clock cover 16 consecutive rows at one chunk; XOR-ing the
-// chunk with the row's window index spreads those rows over all 16 bank groups.
+// K tile (16-byte row reads only): a row-read pass serves the 16 lanes that agree in
+// lane-id bits 0 and 5 (the LDS pass structure measured on this chip; the backward's
+// pair tile describes it), here 8 keys of one parity at one chunk pair.  XOR-ing the chunk with the
+// row's window index puts them in 16 distinct bank groups at D = 128; at D = 64 and 32,
+// where a 256-byte window holds 2 or 4 rows, the rows of one parity share half of the
+// groups and the reads take two passes.  A pair tile (one pass both ways at every D)
+// measured 0.2-1.2% slower at D = 128 and 0.3% faster at D = 32, where the kernel is
+// bound by its softmax VALU work, so the XOR tiles stay.
 template <int D>
 __device__ inline int k_swz(int r) { return (r / Bf16Tile<D>::RPW) & (Bf16Tile<D>::KCH - 1); }
 // The bf16 kernel uses 16x16x32 MFMA tiles: on this chip a stream of them sustains
