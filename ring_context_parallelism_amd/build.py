@@ -26,12 +26,16 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
-# Instruction-scheduler strategy per source (LLVM's AMDGPU machine scheduler).  The
-# bf16 forward runs 2-3% faster under the iterative ILP scheduler and the backward
-# kernels 1.4% faster under the max-ILP one; the fp32 forward is 5-18% slower under
-# either, so it sits in a file of its own with the default.
+# Per-source code-generation flags (LLVM's AMDGPU backend).  The bf16 forward runs 2-3%
+# faster under the iterative ILP instruction scheduler and the backward kernels 1.4%
+# faster under the max-ILP one; the fp32 forward is 5-18% slower under either, so it
+# sits in a file of its own with the default scheduler.  There, MFMA accumulators in
+# VGPRs instead of AGPRs remove ~110 accumulator copies per key tile (the S init, S to
+# the softmax, the O rescale), which cannot overlap the fp32 MFMAs: 2.9% faster on the
+# d = 24 tabular forward.
 SOURCE_FLAGS = {
     "ra_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "ra_fwd_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "ra_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
