@@ -214,13 +214,18 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 
     // The contraction covers KP column pairs: the zero pad columns beyond the true
     // head dim add nothing (at d = 24 stored as 32: 12 MFMAs instead of 16).
+    // Each lane's LDS reads are a per-lane base plus compile-time offsets: K row
+    // blk * 32 + l32 at column kk * 2 + hh, V row blk * 32 + (i / 4) * 8 + hh * 4 + i % 4
+    // at column n * 32 + l32.
+    const float* krd = &kf[buf][l32 * DP + hh];
+    const float* vrd = &vf[buf][hh * 4 * DP + l32];
     f32x16 s[NB];
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       f32x16 acc = {};
 #pragma unroll
       for (int kk = 0; kk < KP; ++kk) {
-        const float kop = kf[buf][(blk * 32 + l32) * DP + kk * 2 + hh];
+        const float kop = krd[blk * 32 * DP + kk * 2];
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kop, qf[kk], acc, 0, 0, 0);
       }
       s[blk] = acc;
@@ -268,8 +273,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
       for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = blk * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-          const float vop = vf[buf][key * DP + n * 32 + l32];
+          const float vop = vrd[(blk * 32 + (i >> 2) * 8 + (i & 3)) * DP + n * 32];
           o_t[n] = __builtin_amdgcn_mfma_f32_32x32x2f32(vop, s[blk][i], o_t[n], 0, 0, 0);
         }
 
