@@ -14,12 +14,14 @@
 // double-buffered.  Scores are computed transposed, S^T = K Q^T, with the fp32
 // 32x32x2 MFMA: every lane holds one query row (the two halves of a wave the same
 // rows, different keys), and the QK^T contraction stops at the true head dim when
-// that leaves a quarter of D as padding.  O^T += V^T P^T takes P^T straight from the
-// score registers, two keys per MFMA.
+// that leaves a quarter of D as padding.  O^T += V^T P^T takes P^T straight from
+// registers, two keys per MFMA.  As in the bf16 kernel, the reference max of the
+// online softmax moves lazily: only a tile whose partial row sums exceed 2^8 pays for
+// the exact row max and the rescale of O and l.
 //
 // This file is compiled apart from the bf16 forward because the two want different
-// instruction schedulers: the default one for this kernel, an ILP-oriented one for
-// the bf16 kernel.
+// code generation: the default instruction scheduler and MFMA accumulators in VGPRs
+// for this kernel, an ILP-oriented scheduler for the bf16 kernel.
 #include "ra_internal.h"
 
 namespace ra {
@@ -31,6 +33,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kMInit = -1.0e30f;  // finite start for the running max (no inf - inf)
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kSumCap = 256.0f;   // bound on a lane's partial row sum of one tile
 constexpr int kThreads = 256;
 constexpr int kBM = kFwdF32BlockM;  // 32 rows per wave
 static_assert(kBM == 32 * (kThreads / 64), "one 32-row MFMA tile per wave");
@@ -40,7 +43,8 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // Row state of the fp32 kernel, whose 32x32 accumulators give every lane one query
 // row and the two halves of a wave the same rows.
 struct RowState {
-  float m;  // running max of raw scores (shared by the two halves of a row)
+  float m;  // reference max of raw scores, at most the row max so far (shared by the
+            // two halves of a row); it moves lazily, so exp2((s - m) * scale_log2) <= 2^8
   float l;  // running sum of exp2((s - m) * scale_log2) over this lane's keys
 };
 
@@ -112,8 +116,11 @@ __device__ inline void fwd_epilogue(const FwdArgs& a, int b, int h, int tq, int 
 
 // KP: column pairs of the QK^T contraction, D / 2, or 3 D / 8 when the true head dim
 // is at most 3 D / 4 (the remaining columns are zero padding).
+// Workgroups per CU the register allocation must allow: 4 at D = 32 (128 VGPRs; a few
+// loop-invariant values spill and are reloaded once to three times per key tile, and
+// the kernel still measured 1% faster than at 3 per CU), else 2.
 template <int D, int BN, bool PK, int KP>
-__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, D == 32 ? 4 : 2) void fwd_f32_kernel(FwdArgs a) {
   constexpr int DP = D + 1;            // padded LDS row (conflict-free column reads)
   constexpr int NB = BN / 32;
   constexpr int ND = D / 32;
@@ -242,28 +249,42 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
           if ((uint32_t)(u - kv_lo) >= width) s[blk][i] = kNegInf;
         }
     }
-    float mx = s[0][0];
+    f32x16 p[NB];
+    auto expo = [&]() {
+      const float mc = st.m * a.scale_log2;
+      float ls[2] = {0.0f, 0.0f};
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk)
+      for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[blk][i]);
-    mx = pair_max(mx);
-    const float m_new = fmaxf(st.m, mx);
-    const float alpha = fast_exp2((st.m - m_new) * a.scale_log2);
-    st.m = m_new;
-    const float mc = m_new * a.scale_log2;
-    float lsum = 0.0f;
+        for (int i = 0; i < 16; ++i) {
+          const float pv = fast_exp2(__builtin_fmaf(s[blk][i], a.scale_log2, -mc));
+          ls[i & 1] += pv;
+          p[blk][i] = pv;
+        }
+      return ls[0] + ls[1];
+    };
+    // P against the current reference max first; every p is at most its lane's
+    // partial row sum, so while the partials of a row stay <= 2^8 the reference may
+    // stay.  Otherwise (the first visible tile, or a row whose max rose) the wave
+    // finds the exact row max, rescales O and l, and takes P again.
+    float part = expo();
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(part <= kSumCap)) != 0, 0)) {
+      float v = kNegInf;
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk)
+      for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(__builtin_fmaf(s[blk][i], a.scale_log2, -mc));
-        lsum += pv;
-        s[blk][i] = pv;
-      }
-    st.l = st.l * alpha + lsum;
+        for (int i = 0; i < 16; ++i) v = fmaxf(v, s[blk][i]);
+      const float mx = pair_max(v);
+      const bool reset = !(pair_max(part) <= kSumCap);
+      const float m_new = reset ? fmaxf(mx, st.m) : st.m;
+      const float alpha = fast_exp2((st.m - m_new) * a.scale_log2);
+      st.m = m_new;
+      st.l *= alpha;
 #pragma unroll
-    for (int n = 0; n < ND; ++n) o_t[n] *= alpha;
+      for (int n = 0; n < ND; ++n) o_t[n] *= alpha;
+      part = expo();
+    }
+    st.l += part;
 
     // O^T += V^T P^T with K = 2 per MFMA: step i pairs the keys the two halves of
     // the wave hold in accumulator slot i.
@@ -274,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float vop = vrd[(blk * 32 + (i >> 2) * 8 + (i & 3)) * DP + n * 32];
-          o_t[n] = __builtin_amdgcn_mfma_f32_32x32x2f32(vop, s[blk][i], o_t[n], 0, 0, 0);
+          o_t[n] = __builtin_amdgcn_mfma_f32_32x32x2f32(vop, p[blk][i], o_t[n], 0, 0, 0);
         }
 
     if (j + 1 < n_tiles) store(buf ^ 1);
