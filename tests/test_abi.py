@@ -204,3 +204,18 @@ def test_noalloc_refuses_a_workspace_beyond_the_static_array_before_any_launch()
     # the problem checks come first
     assert _status_of(ra.ra_ring_bwd_noalloc, _prob(world=0), 0, FAKE, ks, ks, FAKE, FAKE, FAKE,
                       FAKE, ks, ks, 0) == ra.RA_ERR_SHAPE
+
+
+def test_build_flags_name_real_sources():
+    """Per-source code-generation flags are keyed by file name: a key that names no
+    source, or a source that is not on disk, would silently build without them."""
+    from ring_context_parallelism_amd import build
+    assert set(build.SOURCE_FLAGS) <= set(build.SOURCES)
+    for src in build.SOURCES:
+        assert os.path.exists(os.path.join(build.CSRC, src)), src
+    for flags in build.SOURCE_FLAGS.values():
+        assert all(isinstance(f, str) and f for f in flags)
+        # every -mllvm takes exactly one backend option after it
+        for k, f in enumerate(flags):
+            if f == "-mllvm":
+                assert k + 1 < len(flags) and flags[k + 1].startswith("-amdgpu-")
