@@ -85,6 +85,9 @@ MOVING_MAX = [
     _wl("bf16", 64, 64, "zigzag", 2, 1040, False, 1, 2, 2, seed=121),
     _wl("bf16", 32, 24, "striped", 2, 1000, True, 1, 2, 1, dist="uniform", scale=1.0, seed=122),
     _wl("f32", 64, 64, "striped", 2, 1024, True, 1, 1, 1, seed=123),
+    # fp32 at both contraction lengths: d = 24 in 32 columns (three quarters) and d = 128
+    _wl("f32", 32, 24, "zigzag", 2, 1000, True, 1, 2, 1, dist="uniform", scale=1.0, seed=124),
+    _wl("f32", 128, 128, "contiguous", 2, 900, True, 1, 2, 2, seed=125),
 ]
 
 
