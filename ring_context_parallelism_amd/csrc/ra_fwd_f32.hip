@@ -10,8 +10,8 @@
 //
 // Work decomposition (gfx950, wave64): one workgroup = 4 waves = 128 query rows of
 // one (batch, query head), 32 rows per wave.  K and V tiles are staged row-major in
-// LDS (rows padded by one float, so column reads are conflict-free) through registers,
-// double-buffered.  Scores are computed transposed, S^T = K Q^T, with the fp32
+// LDS (rows padded by one float, so column reads are conflict-free) through registers
+// (buffer loads, rows past the chunk end reading as zeros), double-buffered.  Scores are computed transposed, S^T = K Q^T, with the fp32
 // 32x32x2 MFMA: every lane holds one query row (the two halves of a wave the same
 // rows, different keys), and the QK^T contraction stops at the true head dim when
 // that leaves a quarter of D as padding.  O^T += V^T P^T takes P^T straight from
@@ -39,6 +39,10 @@ constexpr int kBM = kFwdF32BlockM;  // 32 rows per wave
 static_assert(kBM == 32 * (kThreads / 64), "one 32-row MFMA tile per wave");
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
 
 // Row state of the fp32 kernel, whose 32x32 accumulators give every lane one query
 // row and the two halves of a wave the same rows.
@@ -116,9 +120,8 @@ __device__ inline void fwd_epilogue(const FwdArgs& a, int b, int h, int tq, int 
 
 // KP: column pairs of the QK^T contraction, D / 2, or 3 D / 8 when the true head dim
 // is at most 3 D / 4 (the remaining columns are zero padding).
-// Workgroups per CU the register allocation must allow: 4 at D = 32 (128 VGPRs; a few
-// loop-invariant values spill and are reloaded once to three times per key tile, and
-// the kernel still measured 1% faster than at 3 per CU), else 2.
+// Workgroups per CU the register allocation must allow: 4 at D = 32 (at most 128
+// VGPRs; it measured 1% faster than at 3 per CU), else 2.
 template <int D, int BN, bool PK, int KP>
 __global__ __launch_bounds__(kThreads, D == 32 ? 4 : 2) void fwd_f32_kernel(FwdArgs a) {
   constexpr int DP = D + 1;            // padded LDS row (conflict-free column reads)
@@ -179,35 +182,39 @@ __global__ __launch_bounds__(kThreads, D == 32 ? 4 : 2) void fwd_f32_kernel(FwdA
 #pragma unroll
   for (int n = 0; n < ND; ++n) o_t[n] = f32x16{};
 
+  // K and V rows through buffer resources sized to the head's L rows: a row past the
+  // chunk end reads as zeros (the host keeps L + 256 rows of bytes below 4 GiB, so the
+  // 32-bit offsets of the last tile do not wrap).
+  static_assert(NCH % kThreads == 0, "whole loads per thread");
+  const uint32_t row_bytes = (uint32_t)(a.kv_st * 4);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, (uint32_t)L * row_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb, (uint32_t)L * row_bytes);
+  // Thread tid moves 16-byte chunk tid % CPR of row tid / CPR of each RPI-row block: a
+  // per-lane offset plus a wave-uniform one (the tile's and the block's first row).
+  constexpr int CPR = D / 4;            // float4 chunks per row
+  constexpr int RPI = kThreads / CPR;   // rows per load instruction of the workgroup
+  static_assert(kThreads % CPR == 0, "whole rows per load instruction");
+  const uint32_t ld_lane = (uint32_t)(tid / CPR) * row_bytes + (uint32_t)(tid % CPR) * 16u;
+  const int st_lane = (tid / CPR) * DP + (tid % CPR) * 4;
   f32x4 sk[NL], sv[NL];
   auto load = [&](int u0) {
 #pragma unroll
     for (int it = 0; it < NL; ++it) {
-      const int ci = it * kThreads + tid;
-      const int r = ci / (D / 4), c = ci % (D / 4);
-      const int u = u0 + r;
-      f32x4 zk = {}, zv = {};
-      if (ci < NCH && u < L) {
-        zk = *(const f32x4*)(kb + (int64_t)u * a.kv_st + c * 4);
-        zv = *(const f32x4*)(vb + (int64_t)u * a.kv_st + c * 4);
-      }
-      sk[it] = zk;
-      sv[it] = zv;
+      const uint32_t soff = (uint32_t)(u0 + it * RPI) * row_bytes;
+      sk[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, ld_lane, soff, 0));
+      sv[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, ld_lane, soff, 0));
     }
   };
   auto store = [&](int buf) {
+    float* kd = &kf[buf][st_lane];
+    float* vd = &vf[buf][st_lane];
 #pragma unroll
-    for (int it = 0; it < NL; ++it) {
-      const int ci = it * kThreads + tid;
-      const int r = ci / (D / 4), c = ci % (D / 4);
-      if (ci < NCH) {
+    for (int it = 0; it < NL; ++it)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kf[buf][r * DP + c * 4 + e] = sk[it][e];
-          vf[buf][r * DP + c * 4 + e] = sv[it][e];
-        }
+      for (int e = 0; e < 4; ++e) {
+        kd[it * RPI * DP + e] = sk[it][e];
+        vd[it * RPI * DP + e] = sv[it][e];
       }
-    }
   };
   if (n_tiles > j0) {
     load(j0 * BN);
