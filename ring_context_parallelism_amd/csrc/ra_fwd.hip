@@ -28,14 +28,6 @@
 namespace ra {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kMInit = -1.0e30f;  // finite start for the running max (no inf - inf)
-constexpr float kLn2 = 0.69314718055994530942f;
-
 // Waves per bf16 workgroup (32 query rows each).  At D = 128 a workgroup of 8 waves
 // (256 rows) shares each K/V tile between twice the rows, which measured 2-6% faster
 // than 4 waves on dense sequences; with packed documents the 4-wave workgroup is
@@ -55,7 +47,6 @@ struct Bf16Cfg {
   static_assert(NW % HG == 0, "whole waves per head");
 };
 
-__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ------------------------------------------------------------------------- bf16 path
 //
@@ -66,14 +57,7 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // arrive as zeros.  V stays row-major; the PV operand V^T is read with the LDS
 // transpose load (ds_read_b64_tr_b16).
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
 
 template <int D>
 struct Bf16Tile {
@@ -231,7 +215,6 @@ __global__ __launch_bounds__((Bf16Cfg<D, PK, HG>::NT), (Bf16Cfg<D, PK, HG>::NW =
   constexpr int NDT = D / 16;   // 16-row head-dim tiles of O^T
   constexpr int NKT = BN / 16;  // 16-key tiles per KV tile
   constexpr int NC = BN / 32;   // 32-key steps of the PV contraction
-  constexpr float kSumCap = 256.0f;  // lazy rescale bound on a lane's partial sum: p <= 2^8
   __shared__ __attribute__((aligned(16))) __bf16 ks0[BN * D];
   __shared__ __attribute__((aligned(16))) __bf16 ks1[BN * D];
   __shared__ __attribute__((aligned(16))) __bf16 vs0[BN * D];

@@ -27,22 +27,10 @@
 namespace ra {
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kMInit = -1.0e30f;  // finite start for the running max (no inf - inf)
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kSumCap = 256.0f;   // bound on a lane's partial row sum of one tile
 constexpr int kThreads = 256;
 constexpr int kBM = kFwdF32BlockM;  // 32 rows per wave
 static_assert(kBM == 32 * (kThreads / 64), "one 32-row MFMA tile per wave");
 
-__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
 
 // Row state of the fp32 kernel, whose 32x32 accumulators give every lane one query
 // row and the two halves of a wave the same rows.

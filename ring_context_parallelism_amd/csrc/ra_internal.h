@@ -103,6 +103,30 @@ __host__ __device__ inline void query_interval(const LayoutMap& m, int32_t cq, i
 }
 
 #if defined(__HIPCC__)
+// Vector types, constants and small helpers of the kernels.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kMInit = -1.0e30f;  // finite start for the running max (no inf - inf)
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.4426950408889634f;
+// Lazy rescale of the online softmax: a lane's partial row sum of one key tile may
+// reach 2^8 before the reference max must move (so every p <= 2^8).
+constexpr float kSumCap = 256.0f;
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Buffer resource over [base, base + bytes): a load past the end returns zeros.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
 // Workgroup id -> logical work item.  Workgroups are dispatched round-robin over the
 // 8 XCDs, so give every XCD one contiguous range of logical ids: the tiles that share
 // a head (and so its K/V or Q reads) then share that XCD's L2.

@@ -6,9 +6,6 @@
 namespace ra {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-constexpr float kNegInf = -__builtin_huge_valf();
-
 // One row of (o, lse) per group of G lanes; G divides 64 and the grid stride is a
 // multiple of 256, so a row never spans two waves and every lane of a row reads
 // lse_acc before the group leader rewrites it.  The grid is capped and strides over
