@@ -28,6 +28,7 @@ CASES = [
     (_wl("bf16", 64, 64, "striped", 3, 390, True, 1, 2, 1, True), "pad"),
     (_wl("bf16", 128, 128, "striped", 2, 520, True, 2, 8, 2, True), "blhd"),  # GQA group 4
     (_wl("f32", 64, 48, "contiguous", 2, 520, False, 1, 2, 2, False), "blhd"),
+    (_wl("f32", 32, 24, "zigzag", 2, 520, True, 2, 2, 1, False), "pad"),  # d = 24 kernel, padded rows
 ]
 
 
