@@ -178,7 +178,10 @@ __global__ __launch_bounds__(kThreads, D == 32 ? 4 : 2) void fwd_f32_kernel(FwdA
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, (uint32_t)L * row_bytes);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb, (uint32_t)L * row_bytes);
   // Thread tid moves 16-byte chunk tid % CPR of row tid / CPR of each RPI-row block: a
-  // per-lane offset plus a wave-uniform one (the tile's and the block's first row).
+  // per-lane offset plus a wave-uniform one (the tile's and the block's first row).  The
+  // whole offset goes in the VGPR operand, which the buffer bounds check always covers
+  // (whether it also covers the SGPR offset is not something to rely on), so rows past
+  // the chunk end read as zeros.
   constexpr int CPR = D / 4;            // float4 chunks per row
   constexpr int RPI = kThreads / CPR;   // rows per load instruction of the workgroup
   static_assert(kThreads % CPR == 0, "whole rows per load instruction");
@@ -188,9 +191,9 @@ __global__ __launch_bounds__(kThreads, D == 32 ? 4 : 2) void fwd_f32_kernel(FwdA
   auto load = [&](int u0) {
 #pragma unroll
     for (int it = 0; it < NL; ++it) {
-      const uint32_t soff = (uint32_t)(u0 + it * RPI) * row_bytes;
-      sk[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, ld_lane, soff, 0));
-      sv[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, ld_lane, soff, 0));
+      const uint32_t off = ld_lane + (uint32_t)(u0 + it * RPI) * row_bytes;
+      sk[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
+      sv[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
     }
   };
   auto store = [&](int buf) {

@@ -3,7 +3,10 @@
 The problem carries element strides (b, h, t) for q, every k/v chunk and out/dout;
 callers often hold [B, L, H, D] (sequence-major) tensors, or rows padded beyond D.
 These cases stage the same inputs in such layouts and compare the ring forward and
-backward with the fp64 oracle.
+backward with the fp64 oracle.  The "rowpad" layout follows each head's L rows with
+128 rows of NaN: every kernel reads its last, ragged tile through a buffer resource
+bounded at row L, so those rows must read as zeros (a NaN that got in would reach the
+outputs through 0 * NaN).
 """
 import numpy as np
 import pytest
@@ -29,7 +32,10 @@ CASES = [
     (_wl("bf16", 128, 128, "striped", 2, 520, True, 2, 8, 2, True), "blhd"),  # GQA group 4
     (_wl("f32", 64, 48, "contiguous", 2, 520, False, 1, 2, 2, False), "blhd"),
     (_wl("f32", 32, 24, "zigzag", 2, 520, True, 2, 2, 1, False), "pad"),  # d = 24 kernel, padded rows
+    (_wl("f32", 32, 24, "contiguous", 2, 520, False, 1, 2, 2, False), "rowpad"),
+    (_wl("bf16", 128, 128, "zigzag", 2, 600, True, 1, 2, 1, True), "rowpad"),
 ]
+ROW_PAD = 128  # NaN rows after each head's L rows (more than any tile reaches past L)
 
 
 def _ids(c):
@@ -46,6 +52,9 @@ def _place(arr, pos, D, dtype, dev, storage):
     if storage == "blhd":
         buf = torch.zeros((B, L, H, D), dtype=dtype, device=dev)
         view = buf.permute(0, 2, 1, 3)
+    elif storage == "rowpad":
+        buf = torch.full((B, H, L + ROW_PAD, D), float("nan"), dtype=dtype, device=dev)
+        view = buf[:, :, :L]
     else:
         buf = torch.zeros((B, H, L, D + 64), dtype=dtype, device=dev)
         view = buf[..., :D]
@@ -56,6 +65,8 @@ def _place(arr, pos, D, dtype, dev, storage):
 def _empty_like_layout(B, H, L, D, dtype, dev, storage):
     if storage == "blhd":
         return torch.zeros((B, L, H, D), dtype=dtype, device=dev).permute(0, 2, 1, 3)
+    if storage == "rowpad":
+        return torch.full((B, H, L + ROW_PAD, D), float("nan"), dtype=dtype, device=dev)[:, :, :L]
     return torch.zeros((B, H, L, D + 64), dtype=dtype, device=dev)[..., :D]
 
 
