@@ -109,12 +109,6 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return out.view(np.float32)
 
 
-def bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Upper 16 bits of exactly-bf16 fp32 values (the bf16 storage pattern)."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    return (x.view(np.uint32) >> 16).astype(np.uint16)
-
-
 def fold_rows_axis(x: np.ndarray, heads: int) -> np.ndarray:
     """(1, rows, features, embed) -> (features, heads, rows, embed/heads).
 
@@ -183,9 +177,3 @@ def generate(w: Workload):
         out["bounds"] = document_bounds(w)
     return out
 
-
-def generate_small(w: Workload, seed: int | None = None):
-    """Like ``generate`` but draws at the workload's own (possibly resized) shape
-    without the tabular fold (used for the oracle-sized cases)."""
-    w2 = dataclasses.replace(w, fold=None, seed=w.seed if seed is None else seed)
-    return generate(w2)
