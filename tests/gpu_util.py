@@ -6,6 +6,8 @@ import sys
 import numpy as np
 import torch
 
+from ring_context_parallelism_amd.workloads import generate, round_bf16
+
 # Tolerances of the parity gate: bf16 inputs with fp32 accumulation, fp32 problems,
 # and the LSE.  rel_fro (normwise relative error) is an added gate: the absolute
 # bounds alone would pass an all-zero output where |O| is small.
@@ -91,3 +93,20 @@ def sample_heads(H, seed=0):
     rng = np.random.default_rng(seed + 1)
     mid = rng.choice(np.arange(1, H - 1), size=2, replace=False).tolist()
     return sorted({0, H - 1, *mid})
+
+
+def moving_max_inputs(w):
+    """The workload's draw with q_i + 1 in every component and k_j + beta_j / sqrt(d):
+    s_ij grows by about beta_j, with beta ramping 0 -> 40 along the sequence and one key
+    at S/2 + 3 raised by 60, so the row maxima keep moving along the key axis (random
+    inputs settle them on the first tile)."""
+    arrays = generate(w)
+    S, d = w.seq_total, w.head_dim
+    beta = np.linspace(0.0, 40.0, S, dtype=np.float32)
+    beta[S // 2 + 3] += 60.0
+    q = arrays["q"] + 1.0
+    k = arrays["k"] + (beta / np.sqrt(d))[None, None, :, None]
+    if w.dtype == "bf16":
+        q, k = round_bf16(q), round_bf16(k)
+    arrays["q"], arrays["k"] = q.astype(np.float32), k.astype(np.float32)
+    return arrays

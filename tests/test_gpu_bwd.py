@@ -17,7 +17,7 @@ import torch
 import oracle
 from ring_context_parallelism_amd import ra, staging
 from ring_context_parallelism_amd.workloads import WORKLOADS, Workload, generate
-from tests.gpu_util import Guarded, assert_close, assert_lse, need_gpu, say
+from tests.gpu_util import Guarded, assert_close, assert_lse, moving_max_inputs, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -71,6 +71,47 @@ def test_ring_bwd_every_rank(w):
             sk = assert_close(_np(dks[c])[..., :d], dK[:, :, pos], "bf16", f"dK chunk {c} rank {r}")
             sv = assert_close(_np(dvs[c])[..., :d], dV[:, :, pos], "bf16", f"dV chunk {c} rank {r}")
         say(f"  dQ {s}  dK {sk}  dV {sv}")
+
+
+# Scores spread over ~50 units of the exponent with moving row maxima (the forward's
+# moving-max inputs): P = exp(S * scale - LSE) is recomputed from widely different LSEs.
+# Causal only: without a mask every row sees the key raised by 60, its softmax is one-hot
+# and the true gradient vanishes, which leaves a relative error nothing to measure.
+MOVING_MAX = [
+    _wl(128, 128, "zigzag", 2, 600, True, 1, 4, 2, seed=220),
+    _wl(64, 64, "striped", 2, 520, True, 1, 2, 2, seed=221),
+]
+
+
+@pytest.mark.parametrize("w", MOVING_MAX, ids=_ids)
+def test_ring_bwd_moving_max(w):
+    dev = need_gpu()
+    arrays = moving_max_inputs(w)
+    d = w.head_dim
+    for r in range(w.world):
+        say(f"ring_bwd moving max {_ids(w)} rank {r}")
+        share = staging.stage(w, arrays, dev, rank=r)
+        guard = Guarded()
+        out, lse = staging.ring_forward(share, w, rank=r, alloc=guard)
+        dq, dks, dvs = staging.ring_backward(share, w, out, lse, rank=r, alloc=guard)
+        torch.cuda.synchronize()
+        guard.check(f"moving max fwd+bwd rank {r}")
+        rows = oracle.positions(w.layout, w.seq_total, w.world, r)
+        _, LSE = oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal)
+        assert LSE.max() - LSE.min() > 15.0, "the inputs must move the row maxima"
+        dQ, dK, dV = oracle.attention_bwd(arrays["q"], arrays["k"], arrays["v"],
+                                          arrays["do"][:, :, rows], rows, w.causal)
+        assert_close(_np(dq)[..., :d], dQ, "bf16", f"dQ rank {r}")
+        # dK and dV are compared over all keys at once: these inputs leave some chunks'
+        # key gradients at rounding level (their keys get almost no probability), where
+        # a per-chunk normwise relative error would divide by a near-zero norm.
+        gk, gv = np.zeros_like(dK), np.zeros_like(dV)
+        for c in range(w.world):
+            pos = oracle.positions(w.layout, w.seq_total, w.world, c)
+            gk[:, :, pos] = _np(dks[c])[..., :d]
+            gv[:, :, pos] = _np(dvs[c])[..., :d]
+        assert_close(gk, dK, "bf16", f"dK (all keys) rank {r}")
+        assert_close(gv, dV, "bf16", f"dV (all keys) rank {r}")
 
 
 def test_block_bwd_accumulates_and_skips():

@@ -18,9 +18,9 @@ import torch
 
 import oracle
 from ring_context_parallelism_amd import ra, staging
-from ring_context_parallelism_amd.workloads import WORKLOADS, Workload, generate, round_bf16
-from tests.gpu_util import (Guarded, assert_close, assert_lse, need_gpu, sample_heads,
-                            sample_rows, say)
+from ring_context_parallelism_amd.workloads import WORKLOADS, Workload, generate
+from tests.gpu_util import (Guarded, assert_close, assert_lse, moving_max_inputs, need_gpu,
+                            sample_heads, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -91,25 +91,10 @@ MOVING_MAX = [
 ]
 
 
-def _moving_max_inputs(w):
-    """q_i + 1 in every component and k_j + beta_j / sqrt(d): s_ij grows by about beta_j,
-    with beta ramping 0 -> 40 along the sequence and one key at S/2 + 3 raised by 60."""
-    arrays = generate(w)
-    S, d = w.seq_total, w.head_dim
-    beta = np.linspace(0.0, 40.0, S, dtype=np.float32)
-    beta[S // 2 + 3] += 60.0
-    q = arrays["q"] + 1.0
-    k = arrays["k"] + (beta / np.sqrt(d))[None, None, :, None]
-    if w.dtype == "bf16":
-        q, k = round_bf16(q), round_bf16(k)
-    arrays["q"], arrays["k"] = q.astype(np.float32), k.astype(np.float32)
-    return arrays
-
-
 @pytest.mark.parametrize("w", MOVING_MAX, ids=_ids)
 def test_ring_fwd_moving_max(w):
     dev = need_gpu()
-    arrays = _moving_max_inputs(w)
+    arrays = moving_max_inputs(w)
     d = w.head_dim
     for r in range(w.world):
         say(f"moving max {_ids(w)} rank {r}")
