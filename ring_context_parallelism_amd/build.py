@@ -86,26 +86,35 @@ def _wait(item):
 HOST_SOURCES = ["ra_api.cpp"]  # the C ABI's host code: validation, drivers, host helpers
 
 
-def build_host_asan(out_path: str, cxx: str = "g++") -> str:
-    """Links a copy of the library whose host code (HOST_SOURCES) is compiled with
-    AddressSanitizer, reusing build()'s kernel objects (GPU code stays uninstrumented).
-    Load it in a process that preloads the sanitizer runtime."""
+def build_host_sanitized(out_path: str, sanitizer: str = "address", cxx: str = "g++") -> str:
+    """Links a copy of the library whose host code (HOST_SOURCES) is compiled with a
+    sanitizer ("address" or "undefined"), reusing build()'s kernel objects (GPU code stays
+    uninstrumented).  Undefined-behaviour reports abort the process.  An AddressSanitizer
+    copy must be loaded in a process that preloads the sanitizer runtime."""
     build_dir = os.path.join(HERE, "_build")
     kernel_objs = [o for src, o in zip(SOURCES, _objects(build_dir)) if src not in HOST_SOURCES]
     if not all(os.path.exists(o) for o in kernel_objs):
         build()
+    san = [f"-fsanitize={sanitizer}"]
+    if sanitizer == "undefined":
+        san.append("-fno-sanitize-recover=undefined")
     out_dir = os.path.dirname(os.path.abspath(out_path))
     host_objs = []
     for src in HOST_SOURCES:
-        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".asan.o")
-        subprocess.run([cxx, "-fPIC", "-fsanitize=address", "-fno-omit-frame-pointer", "-g", "-O1",
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + f".{sanitizer}.o")
+        subprocess.run([cxx, "-fPIC"] + san + ["-fno-omit-frame-pointer", "-g", "-O1",
                         "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
                         "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c",
                         os.path.join(CSRC, src), "-o", obj], check=True)
         host_objs.append(obj)
-    subprocess.run([cxx, "-shared", "-fsanitize=address", "-o", out_path] + host_objs + kernel_objs +
+    subprocess.run([cxx, "-shared"] + san + ["-o", out_path] + host_objs + kernel_objs +
                    ["-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"], check=True)
     return out_path
+
+
+def build_host_asan(out_path: str, cxx: str = "g++") -> str:
+    """build_host_sanitized with AddressSanitizer."""
+    return build_host_sanitized(out_path, "address", cxx)
 
 
 if __name__ == "__main__":
