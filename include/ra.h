@@ -93,9 +93,9 @@ typedef enum ra_mode_t {
 
 /* The problem one rank solves.  Plain data, copied by value into every launch. */
 typedef struct ra_problem_t {
-  int64_t batch;           /* B >= 1 */
-  int64_t heads_q;         /* Hq >= 1 */
-  int64_t heads_kv;        /* Hkv >= 1, Hq % Hkv == 0 */
+  int64_t batch;           /* 1 <= B < 2^31 */
+  int64_t heads_q;         /* 1 <= Hq < 2^31 */
+  int64_t heads_kv;        /* 1 <= Hkv < 2^31, Hq % Hkv == 0 */
   int64_t head_dim;        /* true d (1..D); sets the default scale */
   int64_t head_dim_padded; /* D in {32, 64, 128} (storage) */
   int64_t seq_total;       /* S; S % p == 0 (S % 2p == 0 for zigzag); S < 2^31;
@@ -106,7 +106,8 @@ typedef struct ra_problem_t {
   int32_t dtype;           /* ra_dtype_t of q, k, v, out, dout */
   float scale;             /* 0 -> 1/sqrt(head_dim) */
   int32_t seg_count;       /* boundaries per batch element (>= 2), or 0: dense */
-  int64_t q_stride[3];     /* (b, h, t) element strides of q */
+  int64_t q_stride[3];     /* (b, h, t) element strides of q; every stride in
+                              [0, 2^48), a multiple of 16 bytes (RA_ERR_SHAPE) */
   int64_t kv_stride[3];    /* (b, h, t) element strides of every k and v chunk */
   int64_t o_stride[3];     /* (b, h, t) element strides of out and dout */
   const int32_t* seg_bounds; /* device int32 [B, seg_count] document boundaries, or NULL */

@@ -39,6 +39,10 @@ ra_status_t check_problem(const ra_problem_t* p) {
   if (p == nullptr) return fail(RA_ERR_NULL, "problem is NULL");
   if (p->batch < 1 || p->heads_q < 1 || p->heads_kv < 1)
     return fail(RA_ERR_SHAPE, "batch, heads_q and heads_kv must be >= 1");
+  // The kernels take them as 32-bit integers; the bound also keeps batch * heads_q
+  // below 2^62, so the size checks below cannot overflow.
+  if (p->batch > INT32_MAX || p->heads_q > INT32_MAX || p->heads_kv > INT32_MAX)
+    return fail(RA_ERR_SHAPE, "batch, heads_q and heads_kv must be < 2^31");
   if (p->heads_q % p->heads_kv != 0)
     return fail(RA_ERR_SHAPE, "heads_q (%lld) must be a multiple of heads_kv (%lld)",
                 (long long)p->heads_q, (long long)p->heads_kv);
@@ -74,6 +78,8 @@ ra_status_t check_problem(const ra_problem_t* p) {
   for (int i = 0; i < 3; ++i)
     for (int j = 0; j < 3; ++j) {
       if (strides[i][j] < 0) return fail(RA_ERR_SHAPE, "%s[%d] is negative", names[i], j);
+      if (strides[i][j] >= (int64_t(1) << 48))  // keeps every product below in range
+        return fail(RA_ERR_SHAPE, "%s[%d] must be < 2^48 elements", names[i], j);
       if ((strides[i][j] * es) % 16 != 0)
         return fail(RA_ERR_SHAPE, "%s[%d] * element size must be a multiple of 16 bytes",
                     names[i], j);
@@ -82,16 +88,17 @@ ra_status_t check_problem(const ra_problem_t* p) {
   // The kernels address rows inside one head with 32-bit buffer offsets (a tile may
   // run up to 256 rows past the chunk end, where loads return zeros); the backward
   // reads dout that way too.
+  // (L + 256) * row bytes >= 2^32, as a division: the product itself may not fit.
   for (int i = 0; i < 3; ++i)
-    if ((L + 256) * strides[i][2] * es >= (int64_t(1) << 32))
+    if (strides[i][2] * es > ((int64_t(1) << 32) - 1) / (L + 256))
       return fail(RA_ERR_UNSUPPORTED, "%s[2] too large: one head's rows must span < 4 GiB",
                   names[i]);
   if ((L + 256) * p->head_dim_padded * 4 >= (int64_t(1) << 32))
     return fail(RA_ERR_UNSUPPORTED, "chunk too long: one head's fp32 rows must span < 4 GiB");
   // Every attention kernel launches at most 2 work-items per query row (or key) of a
   // chunk rounded up to its tile, and one grid dimension holds fewer than 2^32.
-  const int64_t rows = p->batch * p->heads_q;
-  if (rows * (L + 256) >= (int64_t(1) << 31))
+  const int64_t rows = p->batch * p->heads_q;  // < 2^62
+  if (rows > ((int64_t(1) << 31) - 1) / (L + 256))  // rows * (L + 256) >= 2^31
     return fail(RA_ERR_SHAPE,
                 "problem too large for one launch: batch * heads_q * (L + 256) must be < 2^31");
   return RA_OK;

@@ -136,6 +136,11 @@ FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced on thes
     (dict(scale=-1.0), ra.RA_ERR_SHAPE),
     # batch * heads_q * (L + 256) >= 2^31: more work-items than one grid dimension holds
     (dict(batch=1 << 12, heads_q=1 << 10, heads_kv=1 << 10, seq_total=4096), ra.RA_ERR_SHAPE),
+    # sizes whose products once wrapped past the checks: batch * heads_q * (L + 256) and
+    # the strides are now bounded before any multiplication
+    (dict(batch=1 << 31), ra.RA_ERR_SHAPE),
+    (dict(batch=1 << 30, heads_q=1 << 30, heads_kv=1 << 30, seq_total=64), ra.RA_ERR_SHAPE),
+    (dict(kv_stride=(0, 0, 1 << 48)), ra.RA_ERR_SHAPE),
     (dict(seg_bounds=FAKE, seg_count=1), ra.RA_ERR_SHAPE),
     (dict(seg_bounds=FAKE, seg_count=0), ra.RA_ERR_SHAPE),
     (dict(seg_bounds=FAKE + 2, seg_count=4), ra.RA_ERR_SHAPE),
@@ -219,3 +224,106 @@ def test_build_flags_name_real_sources():
         for k, f in enumerate(flags):
             if f == "-mllvm":
                 assert k + 1 < len(flags) and flags[k + 1].startswith("-amdgpu-")
+
+
+# Property-based fuzz of the host validation and size arithmetic (no launches): any
+# problem description, hostile fields and strides included, must come back with a
+# defined status, and a successful size or count must respect its bound.  Under the
+# sanitizer copies of the library (test_abi_asan.py) an overflow or out-of-bounds
+# access in that arithmetic fails the run.
+from hypothesis import HealthCheck, given, settings, strategies as st  # noqa: E402
+
+_I64 = st.one_of(st.integers(-4, 300), st.sampled_from([0, 1, 1 << 20, 1 << 31, 1 << 40,
+                                                        (1 << 62), -(1 << 40)]))
+_STATUSES = {ra.RA_OK, ra.RA_ERR_NULL, ra.RA_ERR_SHAPE, ra.RA_ERR_UNSUPPORTED}
+
+
+def _raw_problem(f):
+    p = ra.Problem()
+    (p.batch, p.heads_q, p.heads_kv, p.head_dim, p.head_dim_padded, p.seq_total) = f[:6]
+    p.world, p.layout, p.causal, p.dtype = f[6], f[7], f[8], f[9]
+    p.scale = f[10]
+    p.seg_count = 0
+    p.seg_bounds = None
+    for i in range(3):
+        p.q_stride[i], p.kv_stride[i], p.o_stride[i] = f[11][i], f[12][i], f[13][i]
+    return p
+
+
+@settings(max_examples=400, deadline=None, suppress_health_check=list(HealthCheck))
+@given(st.tuples(_I64, _I64, _I64, st.sampled_from([0, 24, 32, 64, 100, 128, 129, -1]),
+                 st.sampled_from([0, 32, 64, 96, 128, 256]), _I64,
+                 st.integers(-2, 40), st.integers(-1, 4), st.integers(0, 1), st.integers(-1, 3),
+                 st.sampled_from([0.0, 0.125, -1.0, float("nan"), float("inf")]),
+                 st.tuples(_I64, _I64, _I64), st.tuples(_I64, _I64, _I64),
+                 st.tuples(_I64, _I64, _I64)),
+       st.integers(-3, 45), st.integers(-3, 45))
+def test_validation_fuzz(f, qc, kc):
+    p = _raw_problem(f)
+    lib = ra.lib()
+    n = ctypes.c_size_t(0)
+    s = lib.ra_ring_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    assert s in _STATUSES
+    if s == ra.RA_OK:
+        L = p.seq_total // p.world
+        assert n.value == p.batch * p.heads_q * L * p.head_dim_padded * 4
+    s2 = lib.ra_ring_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    assert s2 in _STATUSES
+    pairs = ctypes.c_int64(-1)
+    s3 = lib.ra_visible_pairs(ctypes.byref(p), qc, kc, ctypes.byref(pairs))
+    assert s3 in _STATUSES
+    if s3 == ra.RA_OK:
+        L = p.seq_total // p.world
+        assert 0 <= pairs.value <= p.batch * L * L
+
+
+_BIG = st.sampled_from([1, 2, 3, 1 << 20, 1 << 31, 1 << 40, 1 << 61])
+
+
+@st.composite
+def _valid_shape_problem(draw):
+    """Every field passes the structural checks; sizes and strides go up to ~2^62, so
+    the size and stride arithmetic of the validation sees hostile magnitudes."""
+    p = ra.Problem()
+    p.head_dim_padded = draw(st.sampled_from([32, 64, 128]))
+    p.head_dim = draw(st.integers(1, p.head_dim_padded))
+    p.heads_kv = draw(_BIG)
+    g = draw(st.sampled_from([1, 2, 4, 8]))
+    p.heads_q = min(p.heads_kv * g, (1 << 62) // g * g)
+    p.heads_kv = p.heads_q // g
+    p.batch = draw(_BIG)
+    p.world = draw(st.integers(1, 8))
+    p.layout = draw(st.integers(0, 2))
+    p.causal = draw(st.integers(0, 1))
+    p.dtype = draw(st.integers(0, 1))
+    p.scale = 0.0
+    div = 2 * p.world if p.layout == ra.RA_LAYOUT_ZIGZAG else p.world
+    k = draw(st.sampled_from([1, 7, 64, 4096, 1 << 20, (1 << 31) // 16]))
+    p.seq_total = min(k * div, ((1 << 31) - 1) // div * div)
+    unit = 8 if p.dtype == ra.RA_BF16 else 4  # 16 bytes of elements
+    stride = st.one_of(st.integers(0, 64).map(lambda x: x * unit),
+                       st.sampled_from([1 << 40, 1 << 60, (1 << 62) - (1 << 62) % unit]))
+    for i in range(3):
+        p.q_stride[i], p.kv_stride[i], p.o_stride[i] = draw(stride), draw(stride), draw(stride)
+    p.seg_count, p.seg_bounds = 0, None
+    return p
+
+
+@settings(max_examples=400, deadline=None, suppress_health_check=list(HealthCheck))
+@given(_valid_shape_problem(), st.integers(0, 7), st.integers(0, 7))
+def test_validation_fuzz_hostile_sizes(p, qc, kc):
+    lib = ra.lib()
+    n = ctypes.c_size_t(0)
+    s = lib.ra_ring_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    assert s in _STATUSES
+    if s == ra.RA_OK:
+        L = p.seq_total // p.world
+        assert (p.batch * p.heads_q * (L + 256)) < (1 << 31)
+        assert n.value == p.batch * p.heads_q * L * p.head_dim_padded * 4
+    pairs = ctypes.c_int64(-1)
+    s3 = lib.ra_visible_pairs(ctypes.byref(p), min(qc, p.world - 1), min(kc, p.world - 1),
+                              ctypes.byref(pairs))
+    assert s3 in _STATUSES
+    if s3 == ra.RA_OK:
+        L = p.seq_total // p.world
+        assert 0 <= pairs.value <= p.batch * L * L
