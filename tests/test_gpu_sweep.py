@@ -1,0 +1,129 @@
+"""GPU parity on a seeded random sweep of problem shapes, through the C ABI.
+
+The fixed case lists elsewhere pick shapes by hand; here a seeded generator draws them:
+layout, ring size p = 1..4, chunk lengths from 1 to ~260 tokens (ragged against every
+tile size) and, in a quarter of the cases, up to ~1,100 tokens (several workgroups and
+key tiles per chunk, at batch 1 and at most 4 query heads, so the oracle stays quick),
+batch 1-2, GQA groups of 1, 2, 4 and 8, head dims 32/64/128 with the true
+head dim anywhere from half the stored one up to all of it, causal or not, normal or
+uniform values, and packed documents with right padding in about a third of the cases.
+Every rank's share is compared element by element with the oracle:
+
+* the ring forward, bf16 and fp32 (O and LSE);
+* the ring forward + backward, bf16 (dQ of the rank's rows; dK and dV of every KV
+  chunk, gated over all keys together: a chunk that sees a single key has gradients at
+  rounding level, where a per-chunk relative norm measures nothing).
+
+Every output starts as NaN with a NaN guard tail.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ring_context_parallelism_amd import staging
+from ring_context_parallelism_amd.workloads import Workload, generate
+from tests.gpu_util import Guarded, assert_close, assert_lse, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw_cases(n, seed, backward):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = "bf16" if backward or rng.uniform() < 0.65 else "f32"
+        D = int(rng.choice([32, 64, 128]))
+        d = D if rng.uniform() < 0.5 else int(rng.integers(D // 2, D + 1))
+        layout = str(rng.choice(["contiguous", "zigzag", "striped"]))
+        p = int(rng.integers(1, 5))
+        unit = 2 * p if layout == "zigzag" else p
+        long_chunk = rng.uniform() < 0.25
+        L = int(rng.integers(261, 1101)) if long_chunk else int(rng.integers(1, 261))
+        S = max(unit, L * p // unit * unit)
+        causal = bool(rng.uniform() < 0.7)
+        if long_chunk:
+            Hkv, Hq, B = 1, int(rng.choice([1, 2, 4])), 1
+        else:
+            Hkv = int(rng.integers(1, 3))
+            Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+            B = int(rng.integers(1, 3))
+        docs = None
+        if rng.uniform() < 0.33:
+            docs = (int(rng.integers(1, 8)), int(rng.integers(8, S + 9)), float(rng.uniform(0.0, 0.3)))
+        dist, vscale = ("uniform", 1.0) if rng.uniform() < 0.3 else ("normal", 0.5)
+        cases.append(Workload(f"sweep{'b' if backward else 'f'}{i}", 5000 + 100 * backward + i,
+                              dtype, B, Hq, Hkv, d, D, S, p, layout, 0, causal, dist, vscale,
+                              backward=backward, docs=docs))
+    return cases
+
+
+FWD = _draw_cases(80, 77, backward=False)
+BWD = _draw_cases(40, 78, backward=True)
+
+
+def _ids(w):
+    return f"{w.name}-{w.dtype}-D{w.head_dim_padded}d{w.head_dim}-{w.layout}-p{w.world}-" \
+           f"S{w.seq_total}-{'causal' if w.causal else 'full'}-B{w.batch}H{w.heads_q}x" \
+           f"{w.heads_kv}{'-packed' if w.docs else ''}"
+
+
+def _np(t):
+    return t.float().cpu().numpy()
+
+
+def _bounds(arrays):
+    return [list(map(int, b)) for b in arrays["bounds"]] if "bounds" in arrays else None
+
+
+@pytest.mark.parametrize("w", FWD, ids=_ids)
+def test_sweep_ring_fwd_every_rank(w):
+    dev = need_gpu()
+    arrays = generate(w)
+    bounds = _bounds(arrays)
+    d = w.head_dim
+    for r in range(w.world):
+        say(f"sweep ring_fwd {_ids(w)} rank {r}")
+        share = staging.stage(w, arrays, dev, rank=r)
+        guard = Guarded()
+        out, lse = staging.ring_forward(share, w, rank=r, alloc=guard)
+        torch.cuda.synchronize()
+        guard.check(f"ring_fwd rank {r}")
+        rows = oracle.positions(w.layout, w.seq_total, w.world, r)
+        O, LSE = oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal,
+                                      bounds=bounds)
+        got = _np(out)
+        assert_close(got[..., :d], O, w.dtype, f"O rank {r}")
+        assert np.all(got[..., d:] == 0.0), "padded head-dim columns must stay exactly 0"
+        assert np.all(got[np.isneginf(LSE)] == 0.0), "rows that see no key must be exactly 0"
+        assert_lse(_np(lse), LSE, f"LSE rank {r}")
+
+
+@pytest.mark.parametrize("w", BWD, ids=_ids)
+def test_sweep_ring_bwd_every_rank(w):
+    dev = need_gpu()
+    arrays = generate(w)
+    bounds = _bounds(arrays)
+    d = w.head_dim
+    for r in range(w.world):
+        say(f"sweep ring_bwd {_ids(w)} rank {r}")
+        share = staging.stage(w, arrays, dev, rank=r)
+        guard = Guarded()
+        out, lse = staging.ring_forward(share, w, rank=r, alloc=guard)
+        dq, dks, dvs = staging.ring_backward(share, w, out, lse, rank=r, alloc=guard)
+        torch.cuda.synchronize()
+        guard.check(f"ring fwd+bwd rank {r}")
+        rows = oracle.positions(w.layout, w.seq_total, w.world, r)
+        dQ, dK, dV = oracle.attention_bwd(arrays["q"], arrays["k"], arrays["v"],
+                                          arrays["do"][:, :, rows], rows, w.causal, bounds=bounds)
+        got = _np(dq)
+        assert_close(got[..., :d], dQ, "bf16", f"dQ rank {r}")
+        assert np.all(got[..., d:] == 0.0)
+        pos = [oracle.positions(w.layout, w.seq_total, w.world, c) for c in range(w.world)]
+        got_k = np.concatenate([_np(t) for t in dks], axis=2)
+        got_v = np.concatenate([_np(t) for t in dvs], axis=2)
+        want_k = np.concatenate([dK[:, :, p_] for p_ in pos], axis=2)
+        want_v = np.concatenate([dV[:, :, p_] for p_ in pos], axis=2)
+        assert_close(got_k[..., :d], want_k, "bf16", f"dK rank {r}")
+        assert_close(got_v[..., :d], want_v, "bf16", f"dV rank {r}")
+        assert np.all(got_k[..., d:] == 0.0) and np.all(got_v[..., d:] == 0.0)
