@@ -48,7 +48,9 @@
  *    buffers.  seg_bounds = NULL and seg_count = 0 mean one dense sequence.
  *  * Ownership.  The caller owns every buffer and the stream.  The library
  *    allocates nothing, keeps no pointer after returning, and holds no per-call
- *    state; calls on distinct streams are independent.
+ *    state; calls on distinct streams are independent.  The one exception is
+ *    ra_ring_bwd_noalloc: its calls on one GPU share a static device array (see
+ *    its declaration).
  *  * Errors.  Every argument is validated before anything is enqueued; on
  *    failure nothing is written and the status plus ra_last_error() (a
  *    thread-local message) say why.  RA_OK means "enqueued": device faults
