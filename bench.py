@@ -50,7 +50,6 @@ HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "ring_context_parallelism_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_BYTES = 1 << 30
-# kernel key -> (substring of the device function's name, sources it is built from)
 WARM_SECONDS = 0.5  # default untimed warmup work, seconds
 DEFAULT_WORKLOAD = "zigzag_fwdbwd"
 # The forward-only workloads the default run also times (each as one object of the
@@ -59,6 +58,7 @@ OTHER_CONFIGS = ("tiny_fp32", "llama_share", "gqa_striped", "tabular_rows", "tab
 # The packed-document share (forward and backward), reported beside them.
 PACKED_CONFIG = "packed_fwdbwd"
 
+# kernel key -> (substring of the device function's name, sources it is built from)
 KERNELS = {
     "fwd_kernel": ("fwd_bf16_kernel", ("ra_fwd.hip", "ra_internal.h")),
     "fwd_kernel_f32": ("fwd_f32_kernel", ("ra_fwd_f32.hip", "ra_internal.h")),
