@@ -226,7 +226,8 @@ ra_status_t ra_ring_bwd_workspace_size(const ra_problem_t* prob, size_t* bytes);
  * then every step with a visible pair, in ring order: each KV chunk's dk/dv is
  * stored by its step (RA_WRITE), dq is stored by the first live step and added by
  * the others; buffers no live step reaches are zero-filled.  No output needs to be
- * initialised by the caller.  out / lse are the forward's results for this rank.  dk_chunks and dv_chunks are HOST arrays of p device
+ * initialised by the caller.  out / lse are the forward's results for this rank.
+ * dk_chunks and dv_chunks are HOST arrays of p device
  * pointers (fp32 [B, Hkv, L, D]); the result is this rank's share of the
  * gradients (its queries only).  ws: at least ra_ring_bwd_workspace_size()
  * bytes, 256-byte aligned.  Supported: bf16.
