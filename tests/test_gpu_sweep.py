@@ -28,7 +28,7 @@ from tests.gpu_util import Guarded, assert_close, assert_lse, need_gpu, say
 pytestmark = pytest.mark.gpu
 
 
-def _draw_cases(n, seed, backward):
+def _draw_cases(n, seed, backward, prefix="sweep"):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -52,7 +52,7 @@ def _draw_cases(n, seed, backward):
         if rng.uniform() < 0.33:
             docs = (int(rng.integers(1, 8)), int(rng.integers(8, S + 9)), float(rng.uniform(0.0, 0.3)))
         dist, vscale = ("uniform", 1.0) if rng.uniform() < 0.3 else ("normal", 0.5)
-        cases.append(Workload(f"sweep{'b' if backward else 'f'}{i}", 5000 + 100 * backward + i,
+        cases.append(Workload(f"{prefix}{'b' if backward else 'f'}{i}", 5000 + 100 * backward + i,
                               dtype, B, Hq, Hkv, d, D, S, p, layout, 0, causal, dist, vscale,
                               backward=backward, docs=docs))
     return cases
@@ -127,3 +127,81 @@ def test_sweep_ring_bwd_every_rank(w):
         assert_close(got_k[..., :d], want_k, "bf16", f"dK rank {r}")
         assert_close(got_v[..., :d], want_v, "bf16", f"dV rank {r}")
         assert np.all(got_k[..., d:] == 0.0) and np.all(got_v[..., d:] == 0.0)
+
+
+# Non-default strides: the same kind of random shapes, stored sequence-major
+# ([B, L, H, D]), with rows padded past D, or followed by NaN rows past the chunk end
+# (which every load must read as zeros), through ra_ring_fwd and ra_ring_bwd.
+STORAGES = ("blhd", "pad", "rowpad")
+STRIDED = [(w, STORAGES[i % 3]) for i, w in enumerate(
+    _draw_cases(18, 79, backward=False, prefix="strided") +
+    _draw_cases(12, 80, backward=True, prefix="strided"))]
+
+
+def _sid(case):
+    w, st = case
+    return f"{_ids(w)}-{st}"
+
+
+@pytest.mark.parametrize("case", STRIDED, ids=_sid)
+def test_sweep_strided_ring_fwd_bwd(case):
+    from ring_context_parallelism_amd import ra
+    from tests.test_gpu_strides import _empty_like_layout, _place
+    dev = need_gpu()
+    w, storage = case
+    arrays = generate(w)
+    bounds = _bounds(arrays)
+    seg = torch.from_numpy(arrays["bounds"]).to(dev) if bounds is not None else None
+    D, d, L = w.head_dim_padded, w.head_dim, w.chunk_len
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    for r in range(w.world):
+        say(f"sweep strided {_sid(case)} rank {r}")
+        rows = oracle.positions(w.layout, w.seq_total, w.world, r)
+        q, q_st = _place(arrays["q"], rows, D, dt, dev, storage)
+        ks, vs = [], []
+        for c in range(w.world):
+            pos = oracle.positions(w.layout, w.seq_total, w.world, c)
+            k, kv_st = _place(arrays["k"], pos, D, dt, dev, storage)
+            v, _ = _place(arrays["v"], pos, D, dt, dev, storage)
+            ks.append(k)
+            vs.append(v)
+        out = _empty_like_layout(w.batch, w.heads_q, L, D, dt, dev, storage)
+        o_st = tuple(out.stride()[:3])
+        prob = ra.make_problem(batch=w.batch, heads_q=w.heads_q, heads_kv=w.heads_kv,
+                               head_dim=d, head_dim_padded=D, seq_total=w.seq_total,
+                               world=w.world, layout=w.layout, causal=w.causal, dtype=w.dtype,
+                               q_stride=q_st, kv_stride=kv_st, o_stride=o_st, seg_bounds=seg)
+        guard = Guarded()
+        lse = guard((w.batch, w.heads_q, L), torch.float32, dev)
+        ws = torch.empty(ra.ra_ring_workspace_size(prob) // 4, dtype=torch.float32, device=dev)
+        ra.ra_ring_fwd(prob, r, q, ks, vs, out, lse, ws)
+        torch.cuda.synchronize()
+        O, LSE = oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal,
+                                      bounds=bounds)
+        got = _np(out)
+        assert_close(got[..., :d], O, w.dtype, f"O rank {r}")
+        assert np.all(got[..., d:] == 0.0)
+        assert_lse(_np(lse), LSE, f"LSE rank {r}")
+        if not w.backward:
+            guard.check(f"strided fwd rank {r}")
+            continue
+        do, do_st = _place(arrays["do"], rows, D, dt, dev, storage)
+        assert do_st == o_st
+        dq = guard((w.batch, w.heads_q, L, D), torch.float32, dev)
+        dks = [guard((w.batch, w.heads_kv, L, D), torch.float32, dev) for _ in range(w.world)]
+        dvs = [guard((w.batch, w.heads_kv, L, D), torch.float32, dev) for _ in range(w.world)]
+        wsb = torch.empty(ra.ra_ring_bwd_workspace_size(prob) // 4, dtype=torch.float32,
+                          device=dev)
+        ra.ra_ring_bwd(prob, r, q, ks, vs, out, do, lse, dq, dks, dvs, wsb)
+        torch.cuda.synchronize()
+        guard.check(f"strided fwd+bwd rank {r}")
+        dQ, dK, dV = oracle.attention_bwd(arrays["q"], arrays["k"], arrays["v"],
+                                          arrays["do"][:, :, rows], rows, w.causal, bounds=bounds)
+        assert_close(_np(dq)[..., :d], dQ, "bf16", f"dQ rank {r}")
+        pos = [oracle.positions(w.layout, w.seq_total, w.world, c) for c in range(w.world)]
+        got_k = np.concatenate([_np(t) for t in dks], axis=2)
+        got_v = np.concatenate([_np(t) for t in dvs], axis=2)
+        assert_close(got_k[..., :d], np.concatenate([dK[:, :, p_] for p_ in pos], axis=2), "bf16",
+                     f"dK rank {r}")
+        assert_close(got_v[..., :d], np.concatenate([dV[:, :, p_] for p_ in pos], axis=2), "bf16",
+                     f"dV rank {r}")
