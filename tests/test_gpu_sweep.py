@@ -205,3 +205,48 @@ def test_sweep_strided_ring_fwd_bwd(case):
                      f"dK rank {r}")
         assert_close(got_v[..., :d], np.concatenate([dV[:, :, p_] for p_ in pos], axis=2), "bf16",
                      f"dV rank {r}")
+
+
+# Per-step partials on random shapes: RA_WRITE of every (query chunk, KV chunk) pair
+# against the oracle's partial of that pair, and an RA_MERGE chain in ring order
+# against the full result.
+PARTIALS = _draw_cases(24, 81, backward=False, prefix="partial")
+
+
+@pytest.mark.parametrize("w", PARTIALS, ids=_ids)
+def test_sweep_block_fwd_partials_and_merge(w):
+    from ring_context_parallelism_amd import ra
+    dev = need_gpu()
+    arrays = generate(w)
+    bounds = _bounds(arrays)
+    d, D, L = w.head_dim, w.head_dim_padded, w.chunk_len
+    scale = 1.0 / np.sqrt(d)
+    for cq in range(w.world):
+        share = staging.stage(w, arrays, dev, rank=cq)
+        qpos = oracle.positions(w.layout, w.seq_total, w.world, cq)
+        o_acc = torch.zeros((w.batch, w.heads_q, L, D), dtype=torch.float32, device=dev)
+        l_acc = torch.full((w.batch, w.heads_q, L), float("-inf"), dtype=torch.float32, device=dev)
+        for ck in oracle.ring_schedule(cq, w.world):
+            say(f"sweep block_fwd {_ids(w)} q_chunk {cq} kv_chunk {ck}")
+            kpos = oracle.positions(w.layout, w.seq_total, w.world, ck)
+            guard = Guarded()
+            o = guard((w.batch, w.heads_q, L, D), torch.float32, dev)
+            lse = guard((w.batch, w.heads_q, L), torch.float32, dev)
+            ra.ra_block_attn_fwd(share.prob, share.q, cq, share.k_chunks[ck], share.v_chunks[ck],
+                                 ck, o, lse, ra.RA_WRITE)
+            ra.ra_block_attn_fwd(share.prob, share.q, cq, share.k_chunks[ck], share.v_chunks[ck],
+                                 ck, o_acc, l_acc, ra.RA_MERGE)
+            torch.cuda.synchronize()
+            guard.check(f"partial ({cq},{ck})")
+            Op, Lp = oracle.attention_partial(arrays["q"][:, :, qpos], arrays["k"][:, :, kpos],
+                                              arrays["v"][:, :, kpos], qpos, kpos, w.causal,
+                                              scale, w.heads_q, w.heads_kv, bounds=bounds,
+                                              seq_total=w.seq_total)
+            got = _np(o)
+            assert_close(got[..., :d], Op, w.dtype, f"partial ({cq},{ck})")
+            assert np.all(got[np.isneginf(Lp)] == 0.0), "rows with no visible key must be 0"
+            assert_lse(_np(lse), Lp, f"partial LSE ({cq},{ck})")
+        O, LSE = oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], qpos, w.causal,
+                                      bounds=bounds)
+        assert_close(_np(o_acc)[..., :d], O, w.dtype, f"merge chain rank {cq}")
+        assert_lse(_np(l_acc), LSE, f"merge chain LSE rank {cq}")
