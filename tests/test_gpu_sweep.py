@@ -250,3 +250,44 @@ def test_sweep_block_fwd_partials_and_merge(w):
                                       bounds=bounds)
         assert_close(_np(o_acc)[..., :d], O, w.dtype, f"merge chain rank {cq}")
         assert_lse(_np(l_acc), LSE, f"merge chain LSE rank {cq}")
+
+
+# The backward's per-step entry points on random shapes: ra_bwd_prepare plus
+# ra_block_attn_bwd (adding) per ring step, and ra_bwd_delta plus the split halves
+# (RA_WRITE on a buffer's first visit, RA_MERGE after) per ring step, must each give
+# exactly what the ring driver ra_ring_bwd gives: every output element has one writer,
+# so the order of the additions is the same in all three.
+STEPS = _draw_cases(14, 82, backward=True, prefix="steps")
+
+
+@pytest.mark.parametrize("w", STEPS, ids=_ids)
+def test_sweep_bwd_step_entry_points_match_the_driver(w):
+    from ring_context_parallelism_amd import ra
+    dev = need_gpu()
+    arrays = generate(w)
+    L, D = w.chunk_len, w.head_dim_padded
+    for r in range(w.world):
+        say(f"sweep bwd steps {_ids(w)} rank {r}")
+        share = staging.stage(w, arrays, dev, rank=r)
+        out, lse = staging.ring_forward(share, w, rank=r)
+        dq, dks, dvs = staging.ring_backward(share, w, out, lse, rank=r)
+        guard = Guarded()
+        mk = lambda H: guard((w.batch, H, L, D), torch.float32, dev)
+        delta = guard((w.batch, w.heads_q, L), torch.float32, dev)
+        dq_b, dk_b, dv_b = mk(w.heads_q), [mk(w.heads_kv) for _ in range(w.world)], \
+            [mk(w.heads_kv) for _ in range(w.world)]
+        dq_c, dk_c, dv_c = mk(w.heads_q), [mk(w.heads_kv) for _ in range(w.world)], \
+            [mk(w.heads_kv) for _ in range(w.world)]
+        ra.ra_bwd_prepare(share.prob, out, share.do, delta, dq_b, dk_b, dv_b)
+        for s, c in enumerate(oracle.ring_schedule(r, w.world)):
+            args = (share.prob, share.q, r, share.k_chunks[c], share.v_chunks[c], c, share.do,
+                    lse, delta)
+            ra.ra_block_attn_bwd(*args, dq_b, dk_b[c], dv_b[c])
+            ra.ra_block_attn_bwd_dkdv(*args, dk_c[c], dv_c[c], mode=ra.RA_WRITE)
+            ra.ra_block_attn_bwd_dq(*args, dq_c, mode=ra.RA_WRITE if s == 0 else ra.RA_MERGE)
+        torch.cuda.synchronize()
+        guard.check(f"step entry points rank {r}")
+        assert torch.equal(dq_b, dq) and torch.equal(dq_c, dq), "dQ"
+        for c in range(w.world):
+            assert torch.equal(dk_b[c], dks[c]) and torch.equal(dk_c[c], dks[c]), f"dK {c}"
+            assert torch.equal(dv_b[c], dvs[c]) and torch.equal(dv_c[c], dvs[c]), f"dV {c}"
