@@ -256,7 +256,8 @@ def test_sweep_block_fwd_partials_and_merge(w):
 # ra_block_attn_bwd (adding) per ring step, and ra_bwd_delta plus the split halves
 # (RA_WRITE on a buffer's first visit, RA_MERGE after) per ring step, must each give
 # exactly what the ring driver ra_ring_bwd gives: every output element has one writer,
-# so the order of the additions is the same in all three.
+# so the order of the additions is the same in all three.  So must
+# ra_ring_bwd_noalloc, whose calls follow one another on shapes of every size here.
 STEPS = _draw_cases(14, 82, backward=True, prefix="steps")
 
 
@@ -285,9 +286,15 @@ def test_sweep_bwd_step_entry_points_match_the_driver(w):
             ra.ra_block_attn_bwd(*args, dq_b, dk_b[c], dv_b[c])
             ra.ra_block_attn_bwd_dkdv(*args, dk_c[c], dv_c[c], mode=ra.RA_WRITE)
             ra.ra_block_attn_bwd_dq(*args, dq_c, mode=ra.RA_WRITE if s == 0 else ra.RA_MERGE)
+        dq_n, dk_n, dv_n = mk(w.heads_q), [mk(w.heads_kv) for _ in range(w.world)], \
+            [mk(w.heads_kv) for _ in range(w.world)]
+        ra.ra_ring_bwd_noalloc(share.prob, r, share.q, share.k_chunks, share.v_chunks, out,
+                               share.do, lse, dq_n, dk_n, dv_n)
         torch.cuda.synchronize()
         guard.check(f"step entry points rank {r}")
-        assert torch.equal(dq_b, dq) and torch.equal(dq_c, dq), "dQ"
+        assert torch.equal(dq_b, dq) and torch.equal(dq_c, dq) and torch.equal(dq_n, dq), "dQ"
         for c in range(w.world):
-            assert torch.equal(dk_b[c], dks[c]) and torch.equal(dk_c[c], dks[c]), f"dK {c}"
-            assert torch.equal(dv_b[c], dvs[c]) and torch.equal(dv_c[c], dvs[c]), f"dV {c}"
+            for got_k, got_v, how in ((dk_b, dv_b, "block"), (dk_c, dv_c, "split"),
+                                      (dk_n, dv_n, "noalloc")):
+                assert torch.equal(got_k[c], dks[c]), f"dK {c} ({how})"
+                assert torch.equal(got_v[c], dvs[c]), f"dV {c} ({how})"
