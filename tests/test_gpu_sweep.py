@@ -298,3 +298,44 @@ def test_sweep_bwd_step_entry_points_match_the_driver(w):
                                       (dk_n, dv_n, "noalloc")):
                 assert torch.equal(got_k[c], dks[c]), f"dK {c} ({how})"
                 assert torch.equal(got_v[c], dvs[c]), f"dV {c} ({how})"
+
+
+# The ring drivers captured into a HIP graph on random shapes: three replays, with
+# eager work and synchronisations between them, each bit for bit equal to the eager
+# forward + backward (the library records only its own kernels, no memset nodes).
+GRAPHS = _draw_cases(6, 83, backward=True, prefix="graph")
+
+
+@pytest.mark.parametrize("w", GRAPHS, ids=_ids)
+def test_sweep_ring_step_graph_replays_match_eager(w):
+    from ring_context_parallelism_amd import ra
+    from tests.test_gpu_graphs import _buffers, _snapshot, _step
+    dev = need_gpu()
+    share = staging.stage(w, generate(w), dev)
+    ws_f = torch.empty(ra.ra_ring_workspace_size(share.prob) // 4, dtype=torch.float32,
+                       device=dev)
+    ws_b = torch.empty(ra.ra_ring_bwd_workspace_size(share.prob) // 4, dtype=torch.float32,
+                       device=dev)
+    buf = _buffers(w, dev)
+    _step(share, w, buf, ws_f, ws_b)
+    torch.cuda.synchronize()
+    eager = _snapshot(buf)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _step(share, w, buf, ws_f, ws_b)  # warm the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        _step(share, w, buf, ws_f, ws_b)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say(f"sweep graph {_ids(w)} replay {rep}")
+        for t in [buf["out"], buf["lse"], buf["dq"]] + buf["dks"] + buf["dvs"]:
+            t.fill_(float("nan") if t.dtype == torch.float32 else 7.0)  # eager work between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(_snapshot(buf), eager):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager step"
