@@ -339,3 +339,56 @@ def test_sweep_ring_step_graph_replays_match_eager(w):
         torch.cuda.synchronize()
         for a, b in zip(_snapshot(buf), eager):
             assert torch.equal(a, b), f"replay {rep} differs from the eager step"
+
+
+# A softmax scale set in the problem (not 1/sqrt(head_dim)) on random shapes, drawn
+# log-uniformly from [0.05, 0.6]: the ring forward, and for bf16 the backward too.
+def _scaled(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = _draw_cases(n // 2, seed, backward=False, prefix="scale") + \
+        _draw_cases(n - n // 2, seed + 1, backward=True, prefix="scale")
+    return [(w, float(np.exp(rng.uniform(np.log(0.05), np.log(0.6))))) for w in cases]
+
+
+SCALED = _scaled(16, 84)
+
+
+def _scid(case):
+    w, scale = case
+    return f"{_ids(w)}-scale{scale:.3f}"
+
+
+@pytest.mark.parametrize("case", SCALED, ids=_scid)
+def test_sweep_custom_softmax_scale(case):
+    dev = need_gpu()
+    w, scale = case
+    arrays = generate(w)
+    bounds = _bounds(arrays)
+    d = w.head_dim
+    for r in range(w.world):
+        say(f"sweep scale {_scid(case)} rank {r}")
+        share = staging.stage(w, arrays, dev, rank=r)
+        share.prob.scale = scale
+        guard = Guarded()
+        out, lse = staging.ring_forward(share, w, rank=r, alloc=guard)
+        torch.cuda.synchronize()
+        rows = oracle.positions(w.layout, w.seq_total, w.world, r)
+        O, LSE = oracle.attention_fwd(arrays["q"], arrays["k"], arrays["v"], rows, w.causal,
+                                      scale=scale, bounds=bounds)
+        assert_close(_np(out)[..., :d], O, w.dtype, f"O rank {r}")
+        assert_lse(_np(lse), LSE, f"LSE rank {r}")
+        if not w.backward:
+            guard.check(f"scale fwd rank {r}")
+            continue
+        dq, dks, dvs = staging.ring_backward(share, w, out, lse, rank=r, alloc=guard)
+        torch.cuda.synchronize()
+        guard.check(f"scale fwd+bwd rank {r}")
+        dQ, dK, dV = oracle.attention_bwd(arrays["q"], arrays["k"], arrays["v"],
+                                          arrays["do"][:, :, rows], rows, w.causal, scale=scale,
+                                          bounds=bounds)
+        assert_close(_np(dq)[..., :d], dQ, "bf16", f"dQ rank {r}")
+        pos = [oracle.positions(w.layout, w.seq_total, w.world, c) for c in range(w.world)]
+        assert_close(np.concatenate([_np(t) for t in dks], axis=2)[..., :d],
+                     np.concatenate([dK[:, :, p_] for p_ in pos], axis=2), "bf16", f"dK rank {r}")
+        assert_close(np.concatenate([_np(t) for t in dvs], axis=2)[..., :d],
+                     np.concatenate([dV[:, :, p_] for p_ in pos], axis=2), "bf16", f"dV rank {r}")
