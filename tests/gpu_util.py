@@ -39,9 +39,9 @@ def stats(got, ref):
                 rel_fro=float(np.linalg.norm(got - ref) / den) if den > 0 else float(np.linalg.norm(got)))
 
 
-def assert_close(got, ref, dtype, what):
+def assert_close(got, ref, dtype, what, tol=None):
     s = stats(got, ref)
-    tol = TOL[dtype]
+    tol = TOL[dtype] if tol is None else tol
     bad = {k: v for k, v in s.items() if v > tol[k]}
     assert not bad, f"{what}: {s} exceeds {tol}"
     return s
